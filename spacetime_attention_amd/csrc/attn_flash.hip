@@ -1,0 +1,314 @@
+// Flash-style fused attention for the full and spatial passes (bf16, gfx950).
+//
+// Computes o = softmax(scale * q k^T) v per (segment, head) without forming
+// the score matrix: the tiled form that "Video Diffusion Models, in depth"
+// (Step 3) calls mandatory, with an online softmax in fp32 (its "Failure
+// modes" keep softmax in FP32). A segment is a run of L consecutive tokens
+// whose queries see exactly its keys: the whole clip for full 3D attention,
+// one latent frame (Hp*Wp tokens) for the spatial pass.
+//
+// Layout of the work (one workgroup = 4 wavefronts = BM query tokens):
+//  * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
+//    the A operand is a 32-key block of K read from LDS, the B operand the
+//    wave's queries kept in registers for the whole pass. In the result each
+//    lane owns one query column and 16 of its keys, so a row max and a row
+//    sum are register reductions plus one exchange with lane^32
+//    (v_permlane32_swap).
+//  * The probabilities are reused in place as the B operand of
+//    O^T = V^T P^T: the contraction runs over keys, and the order in which
+//    keys feed it is free as long as both operands agree, so the S^T result
+//    registers already hold a valid B operand (no shuffles). V^T comes from
+//    a row-major V tile in LDS through ds_read_b64_tr_b16, which hands each
+//    lane four consecutive keys of one feature column.
+//  * K and V tiles of 64 keys are double-buffered in LDS; the next tile's
+//    global loads are issued before the current tile's products. Chunk-XOR
+//    swizzles keep the K reads (32 rows, one 16-byte chunk each) and the
+//    transposed V reads (8 rows x 64 bytes) free of bank conflicts.
+//  * The running maximum is raised only when a tile's maximum exceeds it by
+//    more than 2^8 in the exp2 domain, so the O^T rescale is skipped on most
+//    tiles; normalising by the sum taken against the same reference keeps
+//    the result exactly softmax.
+//  * Workgroups are numbered so that each XCD gets a contiguous run of
+//    (segment, head, query block) tiles and so shares K/V in its own L2.
+#include "vdit_internal.h"
+
+namespace vdit {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;                // keys per LDS tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
+
+template <int D, int QB>
+struct FlashShape {
+    static constexpr int BM = kWaves * 32 * QB;  // queries per workgroup
+    static constexpr int CH = D / 8;             // 16-byte chunks per row
+    static constexpr int KS = D / 16;            // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;            // 32-row blocks of O^T
+    static constexpr int TILE = kBN * D * 2;     // bytes of one K or V tile
+    static constexpr int LOADS = kBN * CH / kThreads;
+    static_assert(kBN * CH % kThreads == 0, "tile must split evenly over the threads");
+};
+
+// Physical 16-byte chunk of logical chunk c in row r of a K tile: XOR with
+// the row index spreads the 16 rows one b128 read touches over all banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r % (D / 8)); }
+
+// Same for a V tile, read transposed: a ds_read_b64_tr_b16 covers 4
+// consecutive rows x 4 chunks per half-wave, so rows are moved apart by
+// multiples of 4 chunks within each 256-byte bank period.
+template <int D>
+__device__ __forceinline__ int swz_v(int r, int c) {
+    constexpr int CH = D / 8;
+    constexpr int RPP = 256 / (2 * D);  // rows per 256-byte bank period
+    return c ^ (4 * ((r / RPP) % (CH / 4)));
+}
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const lds_u8 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
+}
+
+// max and sum of x over the lane pair (l, l^32).
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    uint16_t *__restrict__ o, int nseg, int L, int heads, float c)
+{
+    using S = FlashShape<D, QB>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * S::TILE];
+    lds_u8 *lds = (lds_u8 *)smem;
+
+    const int nqb = (L + S::BM - 1) / S::BM;
+    const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)(nseg * heads * nqb));
+    const int qblk = (int)(id % nqb);
+    const int hd = (int)((id / nqb) % heads);
+    const int seg = (int)(id / ((uint32_t)nqb * heads));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, col = lane & 31;
+    const int64_t rs = (int64_t)heads * D;  // elements between consecutive tokens
+    const int64_t base = ((int64_t)seg * L * heads + hd) * D;
+    const uint16_t *qp = q + base, *kp = k + base, *vp = v + base;
+    uint16_t *op = o + base;
+
+    // This wave's queries, as B operands of S^T = K Q^T.
+    const int q0 = qblk * S::BM + wave * 32 * QB;
+    bf16x8 qop[QB][S::KS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qi = q0 + qb * 32 + col;
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) {
+            if (qi < L)
+                qop[qb][ks] = *(const bf16x8 *)(qp + qi * rs + 16 * ks + 8 * half);
+            else
+                qop[qb][ks] = (bf16x8){};
+        }
+    }
+
+    u32x4 kreg[S::LOADS], vreg[S::LOADS];
+    auto load_tile = [&](int t0) {
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int ci = tid + kThreads * i;
+            const int r = ci / S::CH, ch = ci % S::CH;
+            const int key = t0 + r;
+            if (key < L) {
+                kreg[i] = *(const u32x4 *)(kp + key * rs + ch * 8);
+                vreg[i] = *(const u32x4 *)(vp + key * rs + ch * 8);
+            } else {
+                kreg[i] = (u32x4){0u, 0u, 0u, 0u};
+                vreg[i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        lds_u8 *kb = lds + buf * 2 * S::TILE;
+        lds_u8 *vb = kb + S::TILE;
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int ci = tid + kThreads * i;
+            const int r = ci / S::CH, ch = ci % S::CH;
+            *(__attribute__((address_space(3))) u32x4 *)(kb + r * D * 2 + swz_k<D>(r, ch) * 16) = kreg[i];
+            *(__attribute__((address_space(3))) u32x4 *)(vb + r * D * 2 + swz_v<D>(r, ch) * 16) = vreg[i];
+        }
+    };
+
+    f32x16 oacc[S::DB][QB];
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = (f32x16){};
+    float mref[QB], lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mref[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+    }
+
+    // Lane-constant parts of the transposed V read: 16-lane group g reads
+    // rows 4*(g/2) + lane%16/4 (+8 for the second half of the k-step), at
+    // feature column 16*(g%2) + 4*(lane%4) of each 32-wide block.
+    const int grp = lane >> 4, gl = lane & 15;
+    const int vrow = 4 * (grp >> 1) + (gl >> 2);
+    const int vcol = 16 * (grp & 1) + 4 * (gl & 3);
+
+    const int ntiles = (L + kBN - 1) / kBN;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < ntiles; ++j) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles) load_tile((j + 1) * kBN);
+        const lds_u8 *kb = lds + buf * 2 * S::TILE;
+        const lds_u8 *vb = kb + S::TILE;
+
+        // Each 32-key block of the tile: S^T = K Q^T, online softmax, then
+        // O^T += V^T P^T. Working per block keeps only 16 scores per query
+        // column live at a time.
+        const int kvalid = L - j * kBN;  // keys of this tile inside the segment
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            f32x16 sacc[QB];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16){};
+#pragma unroll
+            for (int ks = 0; ks < S::KS; ++ks) {
+                const int r = kb2 * 32 + col;
+                const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
+                    kb + r * D * 2 + swz_k<D>(r, 2 * ks + half) * 16);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qb][ks], sacc[qb], 0, 0, 0);
+            }
+
+            // Keys past the end of the segment (last tile only).
+            if (kvalid < kBN) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= kvalid)
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) sacc[qb][r] = -INFINITY;
+                }
+            }
+
+            // Online softmax in the exp2 domain: x = s * scale * log2(e).
+            bf16x8 pop[QB][2];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mx = sacc[qb][0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
+                mx = pair_max(mx) * c;
+                const bool raise = mx > mref[qb] + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(raise)) {
+                    const float mnew = raise ? mx : mref[qb];
+                    const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
+                    mref[qb] = mnew;
+                    lsum[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
+                }
+                const float nm = -mref[qb];
+                float ls = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + e], c, nm));
+                        ls += p[e];
+                    }
+                    u32x4 pk;
+                    pk[0] = pack_bf16x2(p[0], p[1]);
+                    pk[1] = pack_bf16x2(p[2], p[3]);
+                    pk[2] = pack_bf16x2(p[4], p[5]);
+                    pk[3] = pack_bf16x2(p[6], p[7]);
+                    pop[qb][s2] = __builtin_bit_cast(bf16x8, pk);
+                }
+                lsum[qb] += ls;
+            }
+
+            // O^T += V^T P^T over the block's two 16-key steps.
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int r0 = kb2 * 32 + 16 * s2 + vrow;
+#pragma unroll
+                for (int db = 0; db < S::DB; ++db) {
+                    const int dc = db * 32 + vcol;
+                    const bf16x4 lo = lds_read_tr(vb + r0 * D * 2 + swz_v<D>(r0, dc >> 3) * 16 + (dc & 7) * 2);
+                    const bf16x4 hi = lds_read_tr(vb + (r0 + 8) * D * 2 + swz_v<D>(r0 + 8, dc >> 3) * 16 + (dc & 7) * 2);
+                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][s2], oacc[db][qb], 0, 0, 0);
+                }
+            }
+            // The other buffer was released by the barrier that ended the
+            // previous tile, so the prefetched tile can land there now,
+            // which ends the prefetch registers' live range early.
+            if (kb2 == 0 && j + 1 < ntiles) store_tile(buf ^ 1);
+        }
+        __syncthreads();
+    }
+
+    // Normalise and store: lane holds query column `col`, features
+    // db*32 + 8*(r/4) + 4*half + r%4.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float inv = 1.0f / pair_sum(lsum[qb]);
+        const int qi = q0 + qb * 32 + col;
+        if (qi < L) {
+#pragma unroll
+            for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = db * 32 + 8 * r4 + 4 * half;
+                    u32x2 w;
+                    w[0] = pack_bf16x2(oacc[db][qb][4 * r4 + 0] * inv, oacc[db][qb][4 * r4 + 1] * inv);
+                    w[1] = pack_bf16x2(oacc[db][qb][4 * r4 + 2] * inv, oacc[db][qb][4 * r4 + 3] * inv);
+                    *(u32x2 *)(op + qi * rs + d) = w;
+                }
+        }
+    }
+}
+
+template <int D, int QB>
+hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int heads,
+                  float c, hipStream_t s) {
+    using S = FlashShape<D, QB>;
+    const int nqb = (L + S::BM - 1) / S::BM;
+    const uint32_t grid = (uint32_t)nseg * heads * nqb;
+    hipLaunchKernelGGL((flash_fwd_bf16<D, QB>), dim3(grid), dim3(kThreads), 0, s,
+                       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
+                       nseg, L, heads, c);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L,
+                             int heads, int D, float scale_log2e, hipStream_t s) {
+    if (D == 128) return launch<128, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+    if (D == 64) return launch<64, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vdit

@@ -1,0 +1,81 @@
+// Internal declarations shared by the HIP translation units of libvdit.
+// Not part of the public ABI (include/vdit.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vdit {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 <-> fp32 on raw bits. Round-to-nearest-even; NaN stays NaN.
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Maps a hardware workgroup id to a logical tile id so that the workgroups
+// one XCD receives (ids congruent mod 8, dispatched round-robin) form one
+// contiguous run of logical tiles and so share K/V in that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t hw_id, uint32_t total) {
+    const uint32_t nx = 8;
+    const uint32_t xcd = hw_id % nx, local = hw_id / nx;
+    const uint32_t per = total / nx, extra = total % nx;
+    return xcd < extra ? xcd * (per + 1) + local : extra * (per + 1) + (xcd - extra) * per + local;
+}
+
+// ---- launchers (each returns hipGetLastError() after its launch) ----------
+
+// Softmax attention over contiguous segments: nseg segments of L tokens each
+// (segment s covers rows [s*L, (s+1)*L) of the [nseg*L, heads, D] arrays);
+// queries of a segment attend to the keys of the same segment. Full attention
+// is nseg = B, L = N; the spatial pass is nseg = B*T, L = Hp*Wp.
+hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg,
+                             int L, int heads, int D, float scale_log2e, hipStream_t s);
+
+// fp32 attention with a generic key set: query token n of batch b has keys
+// key(m) = kbase(n) + m*kstride, m < nkeys, where for mode 0 (full)
+// kbase = b*N, kstride = 1, nkeys = N; mode 1 (spatial) kbase = b*N + t*HW,
+// kstride = 1, nkeys = HW; mode 2 (temporal) kbase = b*N + p, kstride = HW,
+// nkeys = T.
+hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, int B,
+                           int heads, int T, int HW, int D, int mode, float scale, hipStream_t s);
+
+// Temporal pass in bf16: one wavefront per (b, position, head) sequence of T
+// tokens at stride HW tokens.
+hipError_t launch_temporal_bf16(const void *q, const void *k, const void *v, void *o, int B,
+                                int heads, int T, int HW, int D, float scale_log2e, hipStream_t s);
+
+// Patchify as an implicit-im2col GEMM.
+struct PatchGeom {
+    int B, C, pt, ph, pw, Tl, Hl, Wl, T, Hp, Wp, Dout;
+};
+hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, void *tok,
+                                const PatchGeom &g, hipStream_t s);
+hipError_t launch_patchify_f32(const float *x, const float *w, const float *bias, float *tok,
+                               const PatchGeom &g, hipStream_t s);
+
+// 3D RoPE: per pair j (< D/2) its axis (0 t, 1 h, 2 w) and frequency
+// (fp64 so that the angle can be formed and reduced in fp64).
+struct RopeTable {
+    double freq[128];
+    unsigned char axis[128];
+};
+hipError_t launch_rope_bf16(const void *x, void *y, int B, int heads, int T, int Hp, int Wp, int D,
+                            const RopeTable &tab, hipStream_t s);
+hipError_t launch_rope_f32(const float *x, float *y, int B, int heads, int T, int Hp, int Wp, int D,
+                           const RopeTable &tab, hipStream_t s);
+
+}  // namespace vdit

@@ -1,0 +1,252 @@
+"""GPU parity: every HIP entry point against the fp64 oracle, through the C ABI.
+
+Small shapes are compared element by element over whole outputs; they span
+several key tiles and query blocks and end in ragged tails. The full-size
+workloads (480p full, 480p divided, 720p full, block input) run in the same
+launch configuration as the benchmark and are compared on sampled query rows
+(every row of a sampled query costs the oracle 4*N*head_dim FLOP), or in full
+where the oracle is cheap (temporal pass, patchify, RoPE).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import spacetime_attention_amd as vd
+from synthetic_inputs import WORKLOADS, draw, sample_rows, small_grid
+from tests.parity_util import assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+PASSES = {"full": vd.attn_full, "spatial": vd.attn_spatial, "temporal": vd.attn_temporal}
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _qkv(w, q_scale=1.0):
+    d = w.draw_qkv(q_scale)
+    return d, [to_dev(d[n]) for n in ("q", "k", "v")]
+
+
+# ----------------------------------------------------------------------------
+# Small shapes, whole outputs
+# ----------------------------------------------------------------------------
+
+SMALL = [
+    # (name, B, grid, heads, D)
+    ("ragged_231", 2, (3, 7, 11), 2, 128),
+    ("ragged_d64", 1, (5, 6, 9), 3, 64),
+    ("multi_tile_1000", 1, (4, 10, 25), 2, 128),
+    ("single_frame", 1, (1, 9, 15), 2, 128),
+    ("long_time_40", 1, (40, 2, 3), 2, 128),
+    ("one_token_frames", 2, (7, 1, 1), 2, 128),
+]
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16(case, mode):
+    name, B, grid, heads, D = case
+    _announce(f"small bf16 {name} {mode} B={B} grid={grid} heads={heads} D={D}")
+    w = small_grid(name, B, *grid, heads, D, "bf16", seed=100 + len(name))
+    d, (q, k, v) = _qkv(w)
+    got = to_host(PASSES[mode](q, k, v, grid))
+    torch.cuda.synchronize()
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode)
+    assert_close(got, ref, "bf16", f"{name}/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
+def test_peaky_bf16(mode):
+    # Q and K with standard deviation 4: logits of standard deviation 16,
+    # which exercises the running-maximum updates.
+    grid = (3, 8, 13)
+    _announce(f"peaky bf16 {mode} grid={grid}")
+    w = small_grid("peaky", 1, *grid, 2, 128, "bf16", seed=7)
+    d, (q, k, v) = _qkv(w, q_scale=4.0)
+    got = to_host(PASSES[mode](q, k, v, grid))
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode)
+    assert_close(got, ref, "bf16", f"peaky/{mode}")
+
+
+def test_single_key_sets_are_exact():
+    # T = 1: the temporal key set is the query itself; Hp = Wp = 1: so is the
+    # spatial one. The softmax weight is exactly 1 and the output is V bit for bit.
+    _announce("single-key sets")
+    w = small_grid("t1", 2, 1, 5, 13, 2, 128, "bf16", seed=3)
+    d, (q, k, v) = _qkv(w)
+    assert torch.equal(vd.attn_temporal(q, k, v, (1, 5, 13)), v)
+    w = small_grid("hw1", 2, 9, 1, 1, 2, 128, "bf16", seed=4)
+    d, (q, k, v) = _qkv(w)
+    assert torch.equal(vd.attn_spatial(q, k, v, (9, 1, 1)), v)
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_small_f32(mode, D):
+    grid = (3, 5, 7)
+    _announce(f"small f32 {mode} D={D}")
+    w = small_grid("f32", 2, *grid, 2, D, "f32", seed=11)
+    d, (q, k, v) = _qkv(w)
+    got = to_host(PASSES[mode](q, k, v, grid))
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode)
+    assert_close(got, ref, "f32", f"f32/{mode}/D{D}")
+
+
+def test_deterministic_and_in_bounds():
+    # Two runs agree bit for bit (no LDS race), and guard bands around the
+    # output stay untouched (no stray writes).
+    grid = (3, 7, 11)
+    _announce("determinism and guard bands")
+    w = small_grid("guard", 1, *grid, 2, 128, "bf16", seed=21)
+    d, (q, k, v) = _qkv(w)
+    n = q.numel()
+    for fn in PASSES.values():
+        buf = torch.full((n + 2 * 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+        out = buf[4096:4096 + n].view_as(q)
+        fn(q, k, v, grid, out=out)
+        again = fn(q, k, v, grid)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again)
+        assert bool((buf[:4096] == 7.0).all()) and bool((buf[4096 + n:] == 7.0).all())
+
+
+# ----------------------------------------------------------------------------
+# Tiny video DiT (fp32): patchify, each pass, and time-then-space
+# ----------------------------------------------------------------------------
+
+def test_tiny_dit_f32():
+    w = WORKLOADS["tiny"]
+    _announce("tiny video DiT fp32")
+    d = w.draw_latent()
+    x, wt = to_dev(d["x"]), to_dev(d["w"])
+    grid = (w.T, w.Hp, w.Wp)
+    tok = vd.patchify(x, wt, heads=w.heads, head_dim=w.head_dim)
+    ref_tok = oracle.patchify(d["x"].f32, d["w"].f32)
+    assert tuple(tok.shape) == (1, 256, 64)
+    assert_close(to_host(tok), ref_tok, "f32", "tiny/patchify")
+    # Time then space, q = k = v = tokens split into 2 heads of 32.
+    xs = tok.view(1, 256, 2, 32)
+    got = to_host(vd.divided(xs, grid, order=("temporal", "spatial")))
+    ref = oracle.divided(ref_tok.reshape(1, 256, 2, 32), grid, ("temporal", "spatial"))
+    assert_close(got, ref, "f32", "tiny/time-then-space")
+    for mode, fn in PASSES.items():
+        assert_close(to_host(fn(xs, xs, xs, grid)), oracle.attention(ref_tok.reshape(1, 256, 2, 32),
+                     ref_tok.reshape(1, 256, 2, 32), ref_tok.reshape(1, 256, 2, 32), grid, mode),
+                     "f32", f"tiny/{mode}")
+
+
+# ----------------------------------------------------------------------------
+# RoPE and patchify, small and ragged
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_small(dtype):
+    grid = (5, 7, 9)
+    _announce(f"rope small {dtype}")
+    x = draw(31, [("x", (2, 315, 3, 128), 1.0)], dtype)["x"]
+    xd = to_dev(x)
+    got = to_host(vd.rope3d(xd, grid, (44, 42, 42)))
+    ref = oracle.rope3d(x.f32, grid, (44, 42, 42))
+    assert_close(got, ref, dtype, f"rope/{dtype}")
+    # In place gives the same result.
+    vd.rope3d(xd, grid, (44, 42, 42), out=xd)
+    assert_close(to_host(xd), ref, dtype, f"rope-inplace/{dtype}")
+
+
+def test_rope_other_split():
+    grid = (3, 4, 6)
+    _announce("rope split 12/10/10 at head_dim 32 (fp32)")
+    x = draw(32, [("x", (1, 72, 2, 32), 1.0)], "f32")["x"]
+    got = to_host(vd.rope3d(to_dev(x), grid, (12, 10, 10)))
+    assert_close(got, oracle.rope3d(x.f32, grid, (12, 10, 10)), "f32", "rope/12-10-10")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_patchify_small(dtype):
+    _announce(f"patchify small {dtype}")
+    d = draw(41, [("x", (2, 3, 5, 9, 13), 1.0), ("w", (64, 3, 2, 2, 3), 0.02), ("b", (64,), 0.1)], dtype)
+    x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
+    got = to_host(vd.patchify(x, wt, b, heads=2, head_dim=32))
+    ref = oracle.patchify(d["x"].f32, d["w"].f32, d["b"].f32)
+    assert got.shape == ref.shape == (2, 2 * 4 * 4, 64)
+    assert_close(got, ref, dtype, f"patchify/{dtype}")
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads, sampled
+# ----------------------------------------------------------------------------
+
+def _sampled_attention(wname, mode, stride, q_scale=1.0):
+    w = WORKLOADS[wname]
+    grid = (w.T, w.Hp, w.Wp)
+    _announce(f"{wname} {mode} full size, rows every {stride}")
+    d, (q, k, v) = _qkv(w, q_scale)
+    got = PASSES[mode](q, k, v, grid)
+    rows = sample_rows(w.N, stride, offset=stride // 3)
+    got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode, rows=rows)
+    return assert_close(got_rows, ref, "bf16", f"{wname}/{mode}")
+
+
+def test_480p_full_sampled():
+    _sampled_attention("480p_full", "full", 512)
+
+
+def test_480p_divided_spatial_sampled():
+    _sampled_attention("480p_divided", "spatial", 97)
+
+
+def test_480p_divided_temporal_whole():
+    w = WORKLOADS["480p_divided"]
+    grid = (w.T, w.Hp, w.Wp)
+    _announce("480p divided temporal, every row")
+    d, (q, k, v) = _qkv(w)
+    got = to_host(vd.attn_temporal(q, k, v, grid))
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, "temporal")
+    assert_close(got, ref, "bf16", "480p_divided/temporal")
+
+
+def test_720p_full_sampled():
+    _sampled_attention("720p_full", "full", 4099)
+
+
+def test_block_input_path():
+    """Latent (1,16,21,60,104) -> patchify -> RoPE -> spatial -> temporal."""
+    w = WORKLOADS["block_input"]
+    grid = (w.T, w.Hp, w.Wp)
+    split = w.rope_split
+    _announce("block input path")
+    d = w.draw_latent()
+    x, wt = to_dev(d["x"]), to_dev(d["w"])
+    tok = vd.patchify(x, wt, heads=w.heads, head_dim=w.head_dim)
+    ref_tok = oracle.patchify(d["x"].f32, d["w"].f32)
+    assert_close(to_host(tok), ref_tok, "bf16", "block/patchify")
+
+    x0 = tok.view(1, w.N, w.heads, w.head_dim)
+    r0 = vd.rope3d(x0, grid, split)
+    ref_r0 = oracle.rope3d(ref_tok.reshape(1, w.N, w.heads, w.head_dim), grid, split)
+    assert_close(to_host(r0), ref_r0, "bf16", "block/rope")
+
+    x1 = vd.attn_spatial(r0, r0, x0, grid)
+    r1 = vd.rope3d(x1, grid, split)
+    x2 = vd.attn_temporal(r1, r1, x1, grid)
+    torch.cuda.synchronize()
+
+    # Oracle chain restricted to a few patch positions: their temporal outputs
+    # need the spatial outputs of every frame at those positions.
+    HW = w.Hp * w.Wp
+    positions = np.array([0, 777, HW - 1], dtype=np.int64)
+    rows = (np.arange(w.T)[:, None] * HW + positions[None, :]).reshape(-1)
+    xr = ref_tok.reshape(1, w.N, w.heads, w.head_dim)
+    sp_rows = oracle.attention(ref_r0, ref_r0, xr, grid, "spatial", rows=rows)
+    x1_full = np.zeros_like(xr)
+    x1_full[:, rows] = sp_rows
+    r1_full = oracle.rope3d(x1_full, grid, split)
+    ref_x2 = oracle.attention(r1_full, r1_full, x1_full, grid, "temporal", rows=rows)
+    got_x2 = to_host(x2[:, torch.from_numpy(rows).cuda()])
+    assert_close(to_host(x1[:, torch.from_numpy(rows).cuda()]), sp_rows, "bf16", "block/spatial")
+    assert_close(got_x2, ref_x2, "bf16", "block/spatial-then-temporal")
