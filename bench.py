@@ -1,0 +1,242 @@
+"""Benchmark: one step of the spacetime-attention hot path at the Wan 480p shape.
+
+One step, on synthetic seeded inputs already resident in HBM:
+  1. patchify the block-input latent (1,16,21,60,104) bf16 with a 1x2x2
+     Conv3d to [1, 32760, 1536] tokens (12 heads x 128);
+  2. 3D RoPE [44,42,42] on those tokens (q = k);
+  3. full 3D attention on independent N(0,1) Q/K/V [1, 32760, 12, 128];
+  4. divided attention on the batch-2 (CFG pair) Q/K/V [2, 32760, 12, 128]:
+     the spatial pass (504 frames of 1,560 tokens), then the temporal pass
+     (37,440 sequences of 21 tokens).
+`value` is the step's algorithmic attention FLOP (4*N^2*D per (b, head) for
+full attention, its T*(HW)^2 and (HW)*T^2 parts for the two divided passes)
+divided by the measured step time. Every pass is also reported on its own:
+TFLOP/s against the bf16 matrix-core peak for the full and spatial passes,
+GB/s against HBM for the temporal pass, RoPE and patchify.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense): bf16 matrix cores 2.5 PFLOP/s, which is
+# 256 CUs x 2.4 GHz x 4,096 bf16 FLOP per CU per clock; HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention TFLOP/s + % bf16 MFMA peak (full/spatial), temporal GB/s + % HBM"
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (profiling runs)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run one plain 1 GiB device copy first (HBM counter calibration)")
+    return p.parse_args()
+
+
+def _dev(d):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(d.bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "spacetime_attention_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(kernel_file: str, per_launch_key: str):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, if they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(per_launch_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != _source_hash(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import spacetime_attention_amd as vd
+    from synthetic_inputs import WORKLOADS
+
+    torch.cuda.set_device(0)
+    vd.load_library()
+
+    wf, wd, wb = WORKLOADS["480p_full"], WORKLOADS["480p_divided"], WORKLOADS["block_input"]
+    grid = (wf.T, wf.Hp, wf.Wp)
+    HW = wf.Hp * wf.Wp
+    D, H = wf.head_dim, wf.heads
+
+    t0 = time.time()
+    df = wf.draw_qkv()
+    qf, kf, vf = (_dev(df[n]) for n in ("q", "k", "v"))
+    dd = wd.draw_qkv()
+    qd, kd, vd_ = (_dev(dd[n]) for n in ("q", "k", "v"))
+    dl = wb.draw_latent()
+    lat, wgt = _dev(dl["x"]), _dev(dl["w"])
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    tok = torch.empty((1, wb.N, wb.dim), dtype=torch.bfloat16, device="cuda")
+    rot = torch.empty((1, wb.N, wb.heads, wb.head_dim), dtype=torch.bfloat16, device="cuda")
+    of = torch.empty_like(qf)
+    os_ = torch.empty_like(qd)
+    ot = torch.empty_like(qd)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    passes = ["patchify", "rope", "full", "spatial", "temporal"]
+    ev = {p: [] for p in passes}
+
+    def step(record: bool):
+        def run(name, fn):
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                ev[name].append((a, b))
+            else:
+                fn()
+        run("patchify", lambda: vd.patchify(lat, wgt, heads=wb.heads, head_dim=wb.head_dim, out=tok))
+        run("rope", lambda: vd.rope3d(tok.view(1, wb.N, wb.heads, wb.head_dim), grid, wb.rope_split,
+                                      out=rot))
+        run("full", lambda: vd.attn_full(qf, kf, vf, grid, out=of))
+        run("spatial", lambda: vd.attn_spatial(qd, kd, vd_, grid, out=os_))
+        run("temporal", lambda: vd.attn_temporal(qd, kd, vd_, grid, out=ot))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between two synchronisations. Per-launch events
+    # are recorded on the same stream the library launches on.
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed * 1e3 / args.steps
+
+    def avg_ms(name):
+        return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
+
+    f_full = 4.0 * wf.B * H * wf.N * wf.N * D
+    f_spatial = 4.0 * wd.B * H * wd.T * HW * HW * D
+    f_temporal = 4.0 * wd.B * H * HW * wd.T * wd.T * D
+    b_temporal = 4.0 * wd.B * wd.N * H * D * 2            # read Q, K, V, write O, bf16
+    b_rope = 2.0 * wb.N * wb.dim * 2                       # read and write one tensor
+    b_patch = (np.prod(wb.latent_shape) + np.prod(wb.weight_shape) + wb.N * wb.dim) * 2.0
+    f_patch = 2.0 * wb.N * wb.dim * np.prod(wb.weight_shape[1:])
+    attn_flop = f_full + f_spatial + f_temporal
+
+    t = {p: avg_ms(p) for p in passes}
+    per_pass = {
+        "full": {"ms": t["full"], "tflops": f_full / t["full"] / 1e9,
+                 "frac_bf16_peak": f_full / t["full"] / 1e9 / PEAK_BF16_TFLOPS,
+                 "tokens_per_s": wf.B * wf.N / t["full"] * 1e3},
+        "spatial": {"ms": t["spatial"], "tflops": f_spatial / t["spatial"] / 1e9,
+                    "frac_bf16_peak": f_spatial / t["spatial"] / 1e9 / PEAK_BF16_TFLOPS,
+                    "tokens_per_s": wd.B * wd.N / t["spatial"] * 1e3},
+        "temporal": {"ms": t["temporal"], "gbs": b_temporal / t["temporal"] / 1e6,
+                     "frac_hbm_peak": b_temporal / t["temporal"] / 1e6 / PEAK_HBM_GBS,
+                     "tflops": f_temporal / t["temporal"] / 1e9,
+                     "tokens_per_s": wd.B * wd.N / t["temporal"] * 1e3},
+        "rope": {"ms": t["rope"], "gbs": b_rope / t["rope"] / 1e6,
+                 "frac_hbm_peak": b_rope / t["rope"] / 1e6 / PEAK_HBM_GBS},
+        "patchify": {"ms": t["patchify"], "gbs": b_patch / t["patchify"] / 1e6,
+                     "frac_hbm_peak": b_patch / t["patchify"] / 1e6 / PEAK_HBM_GBS,
+                     "tflops": f_patch / t["patchify"] / 1e9},
+    }
+
+    achieved = f_full / t["full"] / 1e9
+    roofline = {"kernel": "flash_fwd_bf16<128,1,0> (vdit_attn_full, 480p)", "bound": "mfma",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": _traffic("attn_flash.hip", "flash_full_480p")}
+
+    result = {
+        "metric": METRIC,
+        "value": attn_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "wan480p_attention_layer: patchify+RoPE of latent (1,16,21,60,104) -> "
+                        "[1,32760,1536]; full attention [1,32760,12,128]; divided spatial+temporal "
+                        "[2,32760,12,128]",
+            "grid": list(grid), "heads": H, "head_dim": D, "seq_len": wf.N,
+            "batch_full": wf.B, "batch_divided": wd.B, "parallelism": "single GPU",
+        },
+        "passes": per_pass,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(df, wf)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(df, wf):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload:
+    full attention at 480p for every 32nd query token (plus the last) of
+    all 12 heads. Each sampled row costs exactly 4*N*head_dim FLOP."""
+    import oracle
+    from synthetic_inputs import sample_rows
+
+    grid = (wf.T, wf.Hp, wf.Wp)
+    rows = sample_rows(wf.N, 32)
+    q, k, v = df["q"].f32, df["k"].f32, df["v"].f32
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, grid, "full", rows=rows)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * wf.B * wf.heads * rows.size * wf.N * wf.head_dim
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"full attention 480p [1,32760,12,128], {rows.size} query rows "
+                      f"(every 32nd token) x 12 heads, fp64 C oracle"}
+
+
+if __name__ == "__main__":
+    main()

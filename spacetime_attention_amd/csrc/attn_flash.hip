@@ -20,10 +20,15 @@
 //    registers already hold a valid B operand (no shuffles). V^T comes from
 //    a row-major V tile in LDS through ds_read_b64_tr_b16, which hands each
 //    lane four consecutive keys of one feature column.
-//  * K and V tiles of 64 keys are double-buffered in LDS; the next tile's
-//    global loads are issued before the current tile's products. Chunk-XOR
-//    swizzles keep the K reads (32 rows, one 16-byte chunk each) and the
-//    transposed V reads (8 rows x 64 bytes) free of bank conflicts.
+//  * K and V tiles of 64 keys are double-buffered in LDS and filled by
+//    buffer loads that write LDS directly (no staging registers): lane l of a
+//    load lands at byte 16*l of the wave's 1 KB destination, so each lane
+//    fetches the global chunk that belongs at that swizzled LDS slot. The
+//    buffer descriptor's size ends at the segment's last key, so loads past
+//    it return zeros and need no bounds checks. The next tile's loads are
+//    issued before the current tile's products. Chunk-XOR swizzles keep the
+//    K reads (32 rows, one 16-byte chunk each) and the transposed V reads
+//    (8 rows x 64 bytes) free of bank conflicts.
 //  * The running maximum is raised only when a tile's maximum exceeds it by
 //    more than 2^8 in the exp2 domain, so the O^T rescale is skipped on most
 //    tiles; normalising by the sum taken against the same reference keeps
@@ -68,6 +73,14 @@ __device__ __forceinline__ int swz_v(int r, int c) {
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor word 3 for gfx9-family raw (unswizzled) buffers.
+constexpr int kBufferFlags = 0x00020000;
+
+// Wait until this wave's outstanding vector-memory loads (including the
+// ones that write LDS directly) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const lds_u8 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
@@ -83,11 +96,14 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
+// PASS (0 full, 1 spatial) only names the instantiation, so that profiles
+// attribute the two passes separately; the code is the same.
+template <int D, int QB, int PASS>
+__global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ o, int nseg, int L, int heads, float c)
 {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using S = FlashShape<D, QB>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * S::TILE];
     lds_u8 *lds = (lds_u8 *)smem;
@@ -121,31 +137,33 @@ __global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
         }
     }
 
-    u32x4 kreg[S::LOADS], vreg[S::LOADS];
-    auto load_tile = [&](int t0) {
+    // Buffer descriptors over this (segment, head)'s keys and values: the
+    // size stops at the end of key L-1's row, so any row >= L reads as zero.
+    const int nrec = (int)(((int64_t)(L - 1) * rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kp, 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vp, 0, nrec, kBufferFlags);
+    // Per-lane byte offsets (within a tile) of the chunks this lane fetches:
+    // the wave's i-th load fills LDS rows RPL*(wave*LOADS + i) + lane/CH,
+    // physical chunk lane%CH, which holds logical chunk (lane%CH) ^ swizzle.
+    constexpr int RPL = 64 / S::CH;  // rows per wave-wide 1 KB load
+    uint32_t koff[S::LOADS], voff[S::LOADS];
 #pragma unroll
-        for (int i = 0; i < S::LOADS; ++i) {
-            const int ci = tid + kThreads * i;
-            const int r = ci / S::CH, ch = ci % S::CH;
-            const int key = t0 + r;
-            if (key < L) {
-                kreg[i] = *(const u32x4 *)(kp + key * rs + ch * 8);
-                vreg[i] = *(const u32x4 *)(vp + key * rs + ch * 8);
-            } else {
-                kreg[i] = (u32x4){0u, 0u, 0u, 0u};
-                vreg[i] = (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
+    for (int i = 0; i < S::LOADS; ++i) {
+        const int r = RPL * (wave * S::LOADS + i) + lane / S::CH;
+        const int pc = lane % S::CH;
+        koff[i] = (uint32_t)(r * rs * 2 + (pc ^ (swz_k<D>(r, 0))) * 16);
+        voff[i] = (uint32_t)(r * rs * 2 + (pc ^ (swz_v<D>(r, 0))) * 16);
+    }
+    auto load_tile = [&](int t0, int buf) {
         lds_u8 *kb = lds + buf * 2 * S::TILE;
         lds_u8 *vb = kb + S::TILE;
+        const uint32_t so = (uint32_t)((int64_t)t0 * rs * 2);
 #pragma unroll
         for (int i = 0; i < S::LOADS; ++i) {
-            const int ci = tid + kThreads * i;
-            const int r = ci / S::CH, ch = ci % S::CH;
-            *(__attribute__((address_space(3))) u32x4 *)(kb + r * D * 2 + swz_k<D>(r, ch) * 16) = kreg[i];
-            *(__attribute__((address_space(3))) u32x4 *)(vb + r * D * 2 + swz_v<D>(r, ch) * 16) = vreg[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(kb + (wave * S::LOADS + i) * 1024), 16,
+                                                     koff[i], so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(vb + (wave * S::LOADS + i) * 1024), 16,
+                                                     voff[i], so, 0, 0);
         }
     };
 
@@ -169,13 +187,15 @@ __global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
     const int vcol = 16 * (grp & 1) + 4 * (gl & 3);
 
     const int ntiles = (L + kBN - 1) / kBN;
-    load_tile(0);
-    store_tile(0);
+    load_tile(0, 0);
+    wait_vmem();
     __syncthreads();
 
     for (int j = 0; j < ntiles; ++j) {
         const int buf = j & 1;
-        if (j + 1 < ntiles) load_tile((j + 1) * kBN);
+        // The other buffer was released by the barrier that ended the
+        // previous tile: start filling it now.
+        if (j + 1 < ntiles) load_tile((j + 1) * kBN, buf ^ 1);
         const lds_u8 *kb = lds + buf * 2 * S::TILE;
         const lds_u8 *vb = kb + S::TILE;
 
@@ -261,11 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
                         oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][s2], oacc[db][qb], 0, 0, 0);
                 }
             }
-            // The other buffer was released by the barrier that ended the
-            // previous tile, so the prefetched tile can land there now,
-            // which ends the prefetch registers' live range early.
-            if (kb2 == 0 && j + 1 < ntiles) store_tile(buf ^ 1);
         }
+        wait_vmem();  // the next tile has landed in LDS
         __syncthreads();
     }
 
@@ -288,15 +305,16 @@ __global__ __launch_bounds__(kThreads, 1) void flash_fwd_bf16(
                 }
         }
     }
+#endif
 }
 
-template <int D, int QB>
+template <int D, int QB, int PASS>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int heads,
                   float c, hipStream_t s) {
     using S = FlashShape<D, QB>;
     const int nqb = (L + S::BM - 1) / S::BM;
     const uint32_t grid = (uint32_t)nseg * heads * nqb;
-    hipLaunchKernelGGL((flash_fwd_bf16<D, QB>), dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((flash_fwd_bf16<D, QB, PASS>), dim3(grid), dim3(kThreads), 0, s,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
                        nseg, L, heads, c);
     return hipGetLastError();
@@ -305,9 +323,13 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg
 }  // namespace
 
 hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L,
-                             int heads, int D, float scale_log2e, hipStream_t s) {
-    if (D == 128) return launch<128, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s);
-    if (D == 64) return launch<64, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+                             int heads, int D, float scale_log2e, bool spatial, hipStream_t s) {
+    if (D == 128)
+        return spatial ? launch<128, 1, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
+                       : launch<128, 1, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+    if (D == 64)
+        return spatial ? launch<64, 1, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
+                       : launch<64, 1, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
     return hipErrorInvalidValue;
 }
 

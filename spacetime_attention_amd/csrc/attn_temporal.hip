@@ -12,8 +12,10 @@
 // they touch is one contiguous 4*head_dim*2-byte run. The sequence's frames
 // are HW tokens apart; the kernel addresses them in place, so the
 // time<->space permute is never materialised.
-//  * K and V rows of the sequence are staged into the wave's LDS slice with
-//    16-byte loads, zero-filled past T.
+//  * V rows of the sequence are staged into the wave's LDS slice with 16-byte
+//    loads, zero-filled past T; K and Q are read straight into their MFMA
+//    operand registers (each lane one 16-byte piece of a row per k-step), so
+//    a workgroup needs only 4 x 8 KB of LDS and more of them fit on a CU.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32x32 covers T <= 32; T <= 64
 //    uses 2x2 blocks): the matrix-core work is ~2% of the time the pass's
 //    bytes need at HBM speed, and it frees the vector ALUs, which would
@@ -50,7 +52,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D, int KB>
-__global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
+__global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ o, int B, int heads, int T, int HW, float c)
 {
@@ -58,13 +60,12 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int TILE = TP * D * 2; // bytes of one K or V slice
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * 2 * TILE];
+    constexpr int TILE = TP * D * 2; // bytes of one V slice
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * TILE];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = lane >> 5, col = lane & 31;
-    lds_u8 *ks_ = (lds_u8 *)smem + wave * 2 * TILE;
-    lds_u8 *vs_ = ks_ + TILE;
+    lds_u8 *vs_ = (lds_u8 *)smem + wave * TILE;
 
     const int64_t total = (int64_t)B * HW * heads;
     const int64_t sid = (int64_t)blockIdx.x * kWaves + wave;  // head fastest, then position, then b
@@ -76,26 +77,24 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     const int64_t fs = (int64_t)HW * heads * D;  // elements between frames of one sequence
     const int64_t base = ((b * T * HW + p) * heads + hd) * D;
 
-    // Stage K and V rows, zero past T.
+    // Stage V rows, zero past T.
     for (int ci = lane; ci < TP * CH; ci += 64) {
         const int r = ci / CH, ch = ci % CH;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (active && r < T) {
-            kv = *(const u32x4 *)(k + base + r * fs + ch * 8);
-            vv = *(const u32x4 *)(v + base + r * fs + ch * 8);
-        }
-        *(__attribute__((address_space(3))) u32x4 *)(ks_ + r * D * 2 + swz_k<D>(r, ch) * 16) = kv;
+        u32x4 vv = {0u, 0u, 0u, 0u};
+        if (active && r < T) vv = *(const u32x4 *)(v + base + r * fs + ch * 8);
         *(__attribute__((address_space(3))) u32x4 *)(vs_ + r * D * 2 + swz_v<D>(r, ch) * 16) = vv;
     }
-    // Queries as B operands.
-    bf16x8 qop[KB][KS];
+    // Queries as B operands and keys as A operands, zero past T.
+    bf16x8 qop[KB][KS], kop[KB][KS];
 #pragma unroll
     for (int qb = 0; qb < KB; ++qb) {
         const int qi = qb * 32 + col;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            qop[qb][s] = (active && qi < T) ? *(const bf16x8 *)(q + base + qi * fs + 16 * s + 8 * half)
-                                            : (bf16x8){};
+        for (int s = 0; s < KS; ++s) {
+            const bool in = active && qi < T;
+            qop[qb][s] = in ? *(const bf16x8 *)(q + base + qi * fs + 16 * s + 8 * half) : (bf16x8){};
+            kop[qb][s] = in ? *(const bf16x8 *)(k + base + qi * fs + 16 * s + 8 * half) : (bf16x8){};
+        }
     }
     __syncthreads();
 
@@ -108,14 +107,10 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int r = kb * 32 + col;
-            const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-                ks_ + r * D * 2 + swz_k<D>(r, 2 * s + half) * 16);
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < KB; ++qb)
-                sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qb][s], sacc[kb][qb], 0, 0, 0);
-        }
+                sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][s], qop[qb][s], sacc[kb][qb], 0, 0, 0);
 
     // Exact softmax over the T keys of each query column.
     bf16x8 pop[KB][KB][2];
@@ -183,9 +178,9 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
                     oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][kb][s2], oacc[db][qb], 0, 0, 0);
             }
         }
-    __syncthreads();  // every wave is done reading its K slice
+    __syncthreads();  // every wave is done reading its V slice
 
-    // Normalise into the K slice as row-major O rows, then write whole chunks.
+    // Normalise into the V slice as row-major O rows, then write whole chunks.
 #pragma unroll
     for (int qb = 0; qb < KB; ++qb) {
         const float inv = 1.0f / lsum[qb];
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
                 u32x2 w;
                 w[0] = pack_bf16x2(oacc[db][qb][4 * r4 + 0] * inv, oacc[db][qb][4 * r4 + 1] * inv);
                 w[1] = pack_bf16x2(oacc[db][qb][4 * r4 + 2] * inv, oacc[db][qb][4 * r4 + 3] * inv);
-                *(__attribute__((address_space(3))) u32x2 *)(ks_ + qi * D * 2 + swz_k<D>(qi, d >> 3) * 16 +
+                *(__attribute__((address_space(3))) u32x2 *)(vs_ + qi * D * 2 + swz_k<D>(qi, d >> 3) * 16 +
                                                               (d & 7) * 2) = w;
             }
     }
@@ -207,7 +202,7 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
         for (int ci = lane; ci < T * CH; ci += 64) {
             const int r = ci / CH, ch = ci % CH;
             *(u32x4 *)(o + base + r * fs + ch * 8) =
-                *(const __attribute__((address_space(3))) u32x4 *)(ks_ + r * D * 2 + swz_k<D>(r, ch) * 16);
+                *(const __attribute__((address_space(3))) u32x4 *)(vs_ + r * D * 2 + swz_k<D>(r, ch) * 16);
         }
 }
 

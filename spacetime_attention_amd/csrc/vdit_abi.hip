@@ -62,8 +62,8 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
                                              heads, T, HW, D, (int)mode, s, st));
     const float c = (float)((double)s * kLog2e);
     switch (mode) {
-        case kFull: return launch_status(launch_flash_bf16(q, k, v, o, B, T * HW, heads, D, c, st));
-        case kSpatial: return launch_status(launch_flash_bf16(q, k, v, o, B * T, HW, heads, D, c, st));
+        case kFull: return launch_status(launch_flash_bf16(q, k, v, o, B, T * HW, heads, D, c, false, st));
+        case kSpatial: return launch_status(launch_flash_bf16(q, k, v, o, B * T, HW, heads, D, c, true, st));
         default: return launch_status(launch_temporal_bf16(q, k, v, o, B, heads, T, HW, D, c, st));
     }
 }

@@ -21,9 +21,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-// Two fp32 -> packed bf16 pair (lo in bits 0..15), RNE.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Maps a hardware workgroup id to a logical tile id so that the workgroups
@@ -43,7 +46,7 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t hw_id, uint32_t tota
 // queries of a segment attend to the keys of the same segment. Full attention
 // is nseg = B, L = N; the spatial pass is nseg = B*T, L = Hp*Wp.
 hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg,
-                             int L, int heads, int D, float scale_log2e, hipStream_t s);
+                             int L, int heads, int D, float scale_log2e, bool spatial, hipStream_t s);
 
 // fp32 attention with a generic key set: query token n of batch b has keys
 // key(m) = kbase(n) + m*kstride, m < nkeys, where for mode 0 (full)
