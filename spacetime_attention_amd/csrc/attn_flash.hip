@@ -37,6 +37,8 @@
 //    (segment, head, query block) tiles and so shares K/V in its own L2.
 #include "vdit_internal.h"
 
+#include <type_traits>
+
 namespace vdit {
 namespace {
 
@@ -115,7 +117,8 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
     const int seg = (int)(id / ((uint32_t)nqb * heads));
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int half = lane >> 5, col = lane & 31;
     const int64_t rs = (int64_t)heads * D;  // elements between consecutive tokens
     const int64_t base = ((int64_t)seg * L * heads + hd) * D;
@@ -167,6 +170,28 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
         }
     };
 
+    // Per-lane LDS byte offsets of the operand reads, for buffer 0 and key
+    // block 0. Every other read adds a compile-time constant (buffer, key
+    // block, 16-key step, upper 8 rows), which the ds_read offset field holds:
+    //  * K (A of S^T): row col, logical chunk 2*ks + half;
+    //  * V (A of O^T, transposed read): 16-lane group g reads rows
+    //    4*(g/2) + lane%16/4 at feature column db*32 + 16*(g%2) + 4*(lane%4).
+    // The swizzles depend on the row only through bits the constants leave
+    // unchanged, so the constant parts stay additive.
+    uint32_t kofs[S::KS], vofs[S::DB];
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) kofs[ks] = col * D * 2 + swz_k<D>(col, 2 * ks + half) * 16;
+    {
+        const int grp = lane >> 4, gl = lane & 15;
+        const int vrow = 4 * (grp >> 1) + (gl >> 2);
+        const int vcol = 16 * (grp & 1) + 4 * (gl & 3);
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+            const int dc = db * 32 + vcol;
+            vofs[db] = S::TILE + vrow * D * 2 + swz_v<D>(vrow, dc >> 3) * 16 + (dc & 7) * 2;
+        }
+    }
+
     f32x16 oacc[S::DB][QB];
 #pragma unroll
     for (int db = 0; db < S::DB; ++db)
@@ -179,81 +204,72 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
         lsum[qb] = 0.f;
     }
 
-    // Lane-constant parts of the transposed V read: 16-lane group g reads
-    // rows 4*(g/2) + lane%16/4 (+8 for the second half of the k-step), at
-    // feature column 16*(g%2) + 4*(lane%4) of each 32-wide block.
-    const int grp = lane >> 4, gl = lane & 15;
-    const int vrow = 4 * (grp >> 1) + (gl >> 2);
-    const int vcol = 16 * (grp & 1) + 4 * (gl & 3);
-
     const int ntiles = (L + kBN - 1) / kBN;
-    load_tile(0, 0);
-    wait_vmem();
-    __syncthreads();
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int buf = j & 1;
-        // The other buffer was released by the barrier that ended the
-        // previous tile: start filling it now.
-        if (j + 1 < ntiles) load_tile((j + 1) * kBN, buf ^ 1);
-        const lds_u8 *kb = lds + buf * 2 * S::TILE;
-        const lds_u8 *vb = kb + S::TILE;
-
-        // Each 32-key block of the tile: S^T = K Q^T, online softmax, then
-        // O^T += V^T P^T. Working per block keeps only 16 scores per query
-        // column live at a time.
-        const int kvalid = L - j * kBN;  // keys of this tile inside the segment
+    // One 64-key tile held in LDS buffer BUF: S^T for both 32-key blocks,
+    // the online softmax over the tile, then O^T += V^T P^T.
+    auto tile = [&](auto bufc, int j) {
+        constexpr int BUF = decltype(bufc)::value;
+        constexpr uint32_t B0 = BUF * 2 * S::TILE;
+        f32x16 sacc[2][QB];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            f32x16 sacc[QB];
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb] = (f32x16){};
+            for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb] = (f32x16){};
 #pragma unroll
-            for (int ks = 0; ks < S::KS; ++ks) {
-                const int r = kb2 * 32 + col;
+        for (int ks = 0; ks < S::KS; ++ks)
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
                 const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-                    kb + r * D * 2 + swz_k<D>(r, 2 * ks + half) * 16);
+                    lds + kofs[ks] + (B0 + kb2 * 32 * D * 2));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    sacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qb][ks], sacc[qb], 0, 0, 0);
+                    sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
             }
 
-            // Keys past the end of the segment (last tile only).
-            if (kvalid < kBN) {
+        // Keys past the end of the segment (last tile only).
+        const int kvalid = L - j * kBN;
+        if (kvalid < kBN) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
                     if (key >= kvalid)
 #pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) sacc[qb][r] = -INFINITY;
+                        for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb][r] = -INFINITY;
                 }
-            }
+        }
 
-            // Online softmax in the exp2 domain: x = s * scale * log2(e).
-            bf16x8 pop[QB][2];
+        // Online softmax in the exp2 domain: x = s * scale * log2(e).
+        bf16x8 pop[QB][2][2];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = sacc[qb][0];
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = sacc[0][qb][0];
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[qb][r]);
-                mx = pair_max(mx) * c;
-                const bool raise = mx > mref[qb] + kRescaleSlack;
-                if (__builtin_amdgcn_ballot_w64(raise)) {
-                    const float mnew = raise ? mx : mref[qb];
-                    const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
-                    mref[qb] = mnew;
-                    lsum[qb] *= alpha;
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                    for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
-                }
-                const float nm = -mref[qb];
-                float ls = 0.f;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
+            mx = pair_max(mx) * c;
+            const bool raise = mx > mref[qb] + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(raise)) {
+                const float mnew = raise ? mx : mref[qb];
+                const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
+                mref[qb] = mnew;
+                lsum[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
+            }
+            const float nm = -mref[qb];
+            float ls = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     float p[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][8 * s2 + e], c, nm));
+                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
                         ls += p[e];
                     }
                     u32x4 pk;
@@ -261,28 +277,45 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
                     pk[1] = pack_bf16x2(p[2], p[3]);
                     pk[2] = pack_bf16x2(p[4], p[5]);
                     pk[3] = pack_bf16x2(p[6], p[7]);
-                    pop[qb][s2] = __builtin_bit_cast(bf16x8, pk);
+                    pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
                 }
-                lsum[qb] += ls;
-            }
+            lsum[qb] += ls;
+        }
 
-            // O^T += V^T P^T over the block's two 16-key steps.
+        // O^T += V^T P^T over the tile's four 16-key steps.
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int r0 = kb2 * 32 + 16 * s2 + vrow;
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
                 for (int db = 0; db < S::DB; ++db) {
-                    const int dc = db * 32 + vcol;
-                    const bf16x4 lo = lds_read_tr(vb + r0 * D * 2 + swz_v<D>(r0, dc >> 3) * 16 + (dc & 7) * 2);
-                    const bf16x4 hi = lds_read_tr(vb + (r0 + 8) * D * 2 + swz_v<D>(r0 + 8, dc >> 3) * 16 + (dc & 7) * 2);
+                    constexpr int RB = D * 2;  // bytes per row
+                    const uint32_t off = B0 + (kb2 * 32 + 16 * s2) * RB;
+                    const bf16x4 lo = lds_read_tr(lds + vofs[db] + off);
+                    const bf16x4 hi = lds_read_tr(lds + vofs[db] + (off + 8 * RB));
                     const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
-                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][s2], oacc[db][qb], 0, 0, 0);
+                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][kb2][s2], oacc[db][qb], 0, 0, 0);
                 }
-            }
-        }
-        wait_vmem();  // the next tile has landed in LDS
+    };
+
+    load_tile(0, 0);
+    wait_vmem();
+    __syncthreads();
+    // Tiles alternate between the two LDS buffers; the loop body takes one
+    // tile from each so that the buffer is a compile-time constant. The
+    // other buffer was released by the barrier that ended the previous tile,
+    // so the next tile's loads start before this tile's products.
+    for (int j = 0; j < ntiles; j += 2) {
+        if (j + 1 < ntiles) load_tile((j + 1) * kBN, 1);
+        tile(std::integral_constant<int, 0>{}, j);
+        wait_vmem();
+        __syncthreads();
+        if (j + 1 >= ntiles) break;
+        if (j + 2 < ntiles) load_tile((j + 2) * kBN, 0);
+        tile(std::integral_constant<int, 1>{}, j + 1);
+        wait_vmem();
         __syncthreads();
     }
 
