@@ -90,8 +90,10 @@ const char *vdit_status_str(vdit_status_t status);
  *          latent, weight or bias (VDIT_E_ALIAS).
  * The grid must be the strided convolution's: T = Tl/pt, Hp = Hl/ph,
  * Wp = Wl/pw with floor division (a remainder is dropped, as a Conv3d without
- * padding does); otherwise VDIT_E_SHAPE. C*pt*ph*pw must be <= 4096.
- * head_dim: any positive value with heads*head_dim a multiple of 8.
+ * padding does); otherwise VDIT_E_SHAPE. For VDIT_BF16 the patch length
+ * C*pt*ph*pw, rounded up to a multiple of 16, must be <= 512 (else
+ * VDIT_E_SHAPE). head_dim: any positive value with heads*head_dim a multiple
+ * of 8.
  */
 vdit_status_t vdit_patchify(const void *latent, const void *weight, const void *bias,
                             void *tokens, int B, int C, int pt, int ph, int pw,
@@ -114,9 +116,9 @@ vdit_status_t vdit_patchify(const void *latent, const void *weight, const void *
  * for an odd part.
  *
  * x, y : [B, N, heads, head_dim]. y may equal x (in place); partial overlap is
- *        VDIT_E_ALIAS. Angles are evaluated in fp32 from an fp64-exact
- *        frequency table.
- * head_dim: even, <= 256.
+ *        VDIT_E_ALIAS. Each angle is formed and reduced to [-pi, pi] in fp64,
+ *        then its sin/cos are taken in fp32.
+ * head_dim: a multiple of 8, <= 256 (else VDIT_E_HEAD_DIM); theta > 0.
  */
 vdit_status_t vdit_rope3d(const void *x, void *y, int B, int heads, int T, int Hp, int Wp,
                           int head_dim, int d_t, int d_h, int d_w, float theta,
@@ -136,6 +138,8 @@ vdit_status_t vdit_rope3d(const void *x, void *y, int B, int heads, int T, int H
  * scale      : softmax scale; <= 0 selects 1/sqrt(head_dim).
  * head_dim   : VDIT_BF16: 64 or 128; VDIT_F32: 32, 64 or 128
  *              (else VDIT_E_HEAD_DIM).
+ * Size limit : VDIT_BF16 needs one batch's tensor, N*heads*head_dim*2 bytes,
+ *              below 2 GiB (else VDIT_E_SHAPE); 720p at 40 heads is 774 MB.
  */
 vdit_status_t vdit_attn_full(const void *q, const void *k, const void *v, void *o,
                              int B, int heads, int T, int Hp, int Wp, int head_dim,

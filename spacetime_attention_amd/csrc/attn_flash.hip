@@ -42,20 +42,26 @@
 namespace vdit {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;                // keys per LDS tile
+// Wavefronts per workgroup (32 queries each). Every workgroup streams its
+// segment's whole K/V through L2, so more queries per workgroup means fewer
+// re-reads: full attention (long segments) uses 8; the spatial pass (1,560-
+// token frames that stay in L2) uses 4, which wastes less on the ragged
+// last query block.
+constexpr int kFullWaves = 8;
+constexpr int kSpatialWaves = 4;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
 
-template <int D, int QB>
+template <int D, int QB, int NW>
 struct FlashShape {
-    static constexpr int BM = kWaves * 32 * QB;  // queries per workgroup
+    static constexpr int THREADS = NW * 64;
+    static constexpr int BM = NW * 32 * QB;      // queries per workgroup
     static constexpr int CH = D / 8;             // 16-byte chunks per row
     static constexpr int KS = D / 16;            // k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;            // 32-row blocks of O^T
     static constexpr int TILE = kBN * D * 2;     // bytes of one K or V tile
-    static constexpr int LOADS = kBN * CH / kThreads;
-    static_assert(kBN * CH % kThreads == 0, "tile must split evenly over the threads");
+    static constexpr int LOADS = kBN * CH / THREADS;  // 1 KB LDS loads per wave per tensor
+    static_assert(kBN * CH % THREADS == 0, "tile must split evenly over the threads");
 };
 
 // Physical 16-byte chunk of logical chunk c in row r of a K tile: XOR with
@@ -100,13 +106,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // PASS (0 full, 1 spatial) only names the instantiation, so that profiles
 // attribute the two passes separately; the code is the same.
-template <int D, int QB, int PASS>
-__global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
+template <int D, int QB, int NW, int PASS>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ o, int nseg, int L, int heads, float c)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    using S = FlashShape<D, QB>;
+    using S = FlashShape<D, QB, NW>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * S::TILE];
     lds_u8 *lds = (lds_u8 *)smem;
 
@@ -341,13 +347,13 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_bf16(
 #endif
 }
 
-template <int D, int QB, int PASS>
+template <int D, int QB, int NW, int PASS>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int heads,
                   float c, hipStream_t s) {
-    using S = FlashShape<D, QB>;
+    using S = FlashShape<D, QB, NW>;
     const int nqb = (L + S::BM - 1) / S::BM;
     const uint32_t grid = (uint32_t)nseg * heads * nqb;
-    hipLaunchKernelGGL((flash_fwd_bf16<D, QB, PASS>), dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((flash_fwd_bf16<D, QB, NW, PASS>), dim3(grid), dim3(S::THREADS), 0, s,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
                        nseg, L, heads, c);
     return hipGetLastError();
@@ -358,11 +364,11 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg
 hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L,
                              int heads, int D, float scale_log2e, bool spatial, hipStream_t s) {
     if (D == 128)
-        return spatial ? launch<128, 1, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
-                       : launch<128, 1, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+        return spatial ? launch<128, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
+                       : launch<128, 1, kFullWaves, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
     if (D == 64)
-        return spatial ? launch<64, 1, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
-                       : launch<64, 1, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+        return spatial ? launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
+                       : launch<64, 1, kFullWaves, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
     return hipErrorInvalidValue;
 }
 

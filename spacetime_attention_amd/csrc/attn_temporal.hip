@@ -7,31 +7,46 @@
 // ("Video Diffusion Models, in depth", Step 1) a sequence is 21 x 21 scores,
 // so the pass moves 4 bytes of Q/K/V/O per ~10 FLOP and is bound by HBM.
 //
-// One wavefront owns one (b, position, head) sequence; a workgroup's four
-// wavefronts take four consecutive heads of one position, so every token row
-// they touch is one contiguous 4*head_dim*2-byte run. The sequence's frames
+// One wavefront owns one (b, position, head) sequence; a workgroup's
+// wavefronts take consecutive heads of one position. The sequence's frames
 // are HW tokens apart; the kernel addresses them in place, so the
 // time<->space permute is never materialised.
-//  * V rows of the sequence are staged into the wave's LDS slice with 16-byte
-//    loads, zero-filled past T; K and Q are read straight into their MFMA
-//    operand registers (each lane one 16-byte piece of a row per k-step), so
-//    a workgroup needs only 4 x 8 KB of LDS and more of them fit on a CU.
+//  * Q, K and V rows of the sequence go straight from HBM into the wave's
+//    own LDS slice with buffer loads that write LDS (each 1 KB load covers
+//    four whole 256-byte rows, so every request is a full cache line). The
+//    buffer descriptors end at row T-1, so the padding rows read as zeros.
+//    Each wave only ever reads its own slice, so waves never wait for each
+//    other: no workgroup barrier.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32x32 covers T <= 32; T <= 64
 //    uses 2x2 blocks): the matrix-core work is ~2% of the time the pass's
 //    bytes need at HBM speed, and it frees the vector ALUs, which would
 //    otherwise need ~60 TFLOP/s of fp32 FMA for the same products.
 //  * An exact softmax per query column (one exchange with lane^32), then
 //    O^T = V^T P^T with V^T read through ds_read_b64_tr_b16.
-//  * O is staged through LDS and written back as whole 16-byte row chunks.
+//  * O is staged through the Q slice and written back as whole 16-byte row
+//    chunks.
 #include "vdit_internal.h"
 
 namespace vdit {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 2;  // wavefronts per workgroup (each on its own LDS slice)
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer descriptor word 3 for gfx9-family raw (unswizzled) buffers.
+constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads
+// (including the ones that write LDS directly) are still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 0..63");
+    // vmcnt is split over bits [3:0] and [15:14]; expcnt and lgkmcnt stay at
+    // their maximum (no wait).
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 template <int D>
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r % (D / 8)); }
@@ -51,25 +66,38 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int KB>
-__global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
+// QKR: rows of the Q and K slices. With T <= 24, 24 rows suffice: the
+// operand reads of rows 24..31 then fall into the next slice of the same
+// wave (finite data), and land only in key rows that the mask overwrites
+// with -inf and in query columns that are never stored. V always has TP
+// rows, zero past T, because a zero weight times non-finite padding would
+// not be zero.
+template <int D, int KB, int QKR>
+__global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ o, int B, int heads, int T, int HW, float c)
 {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int TP = 32 * KB;      // padded sequence length
     constexpr int CH = D / 8;        // 16-byte chunks per row
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int TILE = TP * D * 2; // bytes of one V slice
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * TILE];
+    constexpr int VT = TP * D * 2;   // bytes of the V slice
+    constexpr int QT = QKR * D * 2;  // bytes of the Q and of the K slice
+    constexpr int RPL = 64 / CH;     // rows per wave-wide 1 KB load
+    static_assert(QKR % RPL == 0 && QKR <= TP, "slice rows must be whole 1 KB loads");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * (2 * QT + VT)];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, col = lane & 31;
-    lds_u8 *vs_ = (lds_u8 *)smem + wave * TILE;
+    lds_u8 *qs_ = (lds_u8 *)smem + wave * (2 * QT + VT);
+    lds_u8 *ks_ = qs_ + QT;
+    lds_u8 *vs_ = ks_ + QT;
 
     const int64_t total = (int64_t)B * HW * heads;
     const int64_t sid = (int64_t)blockIdx.x * kWaves + wave;  // head fastest, then position, then b
-    const bool active = sid < total;
+    if (sid >= total) return;  // whole wave leaves; no barrier follows
     const int hd = (int)(sid % heads);
     const int64_t bp = sid / heads;
     const int64_t p = bp % HW;
@@ -77,40 +105,52 @@ __global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
     const int64_t fs = (int64_t)HW * heads * D;  // elements between frames of one sequence
     const int64_t base = ((b * T * HW + p) * heads + hd) * D;
 
-    // Stage V rows, zero past T.
-    for (int ci = lane; ci < TP * CH; ci += 64) {
-        const int r = ci / CH, ch = ci % CH;
-        u32x4 vv = {0u, 0u, 0u, 0u};
-        if (active && r < T) vv = *(const u32x4 *)(v + base + r * fs + ch * 8);
-        *(__attribute__((address_space(3))) u32x4 *)(vs_ + r * D * 2 + swz_v<D>(r, ch) * 16) = vv;
-    }
-    // Queries as B operands and keys as A operands, zero past T.
-    bf16x8 qop[KB][KS], kop[KB][KS];
+    // Descriptors over this sequence's rows: the size ends at row T-1.
+    const int nrec = (int)(((int64_t)(T - 1) * fs + D) * 2);
+    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, nrec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, nrec, kBufferFlags);
+    // Q and K first, V last: the score products only wait for Q and K, and
+    // V's loads keep streaming under them.
 #pragma unroll
-    for (int qb = 0; qb < KB; ++qb) {
-        const int qi = qb * 32 + col;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const bool in = active && qi < T;
-            qop[qb][s] = in ? *(const bf16x8 *)(q + base + qi * fs + 16 * s + 8 * half) : (bf16x8){};
-            kop[qb][s] = in ? *(const bf16x8 *)(k + base + qi * fs + 16 * s + 8 * half) : (bf16x8){};
-        }
+    for (int i = 0; i < QKR / RPL; ++i) {
+        const int r = RPL * i + lane / CH, pc = lane % CH;
+        const uint32_t off = (uint32_t)(r * fs * 2) + (pc ^ swz_k<D>(r, 0)) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qs_ + i * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(ks_ + i * 1024), 16, off, 0, 0, 0);
     }
-    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TP / RPL; ++i) {
+        const int r = RPL * i + lane / CH, pc = lane % CH;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(vs_ + i * 1024), 16,
+                                                 (uint32_t)(r * fs * 2) + (pc ^ swz_v<D>(r, 0)) * 16, 0, 0, 0);
+    }
+    // Loads complete in issue order: with only the TP/RPL V loads still
+    // outstanding, this wave's Q and K rows are in its LDS slice.
+    wait_vmem_upto<TP / RPL>();
 
-    // S^T = K Q^T.
+    // S^T = K Q^T: K rows as A operands, Q rows as B operands.
     f32x16 sacc[KB][KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int qb = 0; qb < KB; ++qb) sacc[kb][qb] = (f32x16){};
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s) {
+        bf16x8 kop[KB], qop[KB];
+#pragma unroll
+        for (int xb = 0; xb < KB; ++xb) {
+            const int r = xb * 32 + col;
+            const int off = r * D * 2 + swz_k<D>(r, 2 * s + half) * 16;
+            kop[xb] = *(const __attribute__((address_space(3))) bf16x8 *)(ks_ + off);
+            qop[xb] = *(const __attribute__((address_space(3))) bf16x8 *)(qs_ + off);
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int qb = 0; qb < KB; ++qb)
-                sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][s], qop[qb][s], sacc[kb][qb], 0, 0, 0);
+                sacc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb], qop[qb], sacc[kb][qb], 0, 0, 0);
+    }
 
     // Exact softmax over the T keys of each query column.
     bf16x8 pop[KB][KB][2];
@@ -152,6 +192,7 @@ __global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
     }
 
     // O^T = V^T P^T.
+    wait_vmem_upto<0>();  // V has landed
     const int grp = lane >> 4, gl = lane & 15;
     const int vrow = 4 * (grp >> 1) + (gl >> 2);
     const int vcol = 16 * (grp & 1) + 4 * (gl & 3);
@@ -178,9 +219,9 @@ __global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
                     oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][kb][s2], oacc[db][qb], 0, 0, 0);
             }
         }
-    __syncthreads();  // every wave is done reading its V slice
 
-    // Normalise into the V slice as row-major O rows, then write whole chunks.
+    // Normalise into the Q slice (fully consumed above, and LDS accesses of
+    // one wave complete in order) as row-major O rows, then store whole rows.
 #pragma unroll
     for (int qb = 0; qb < KB; ++qb) {
         const float inv = 1.0f / lsum[qb];
@@ -193,25 +234,24 @@ __global__ __launch_bounds__(kWaves * 64, 4) void temporal_bf16(
                 u32x2 w;
                 w[0] = pack_bf16x2(oacc[db][qb][4 * r4 + 0] * inv, oacc[db][qb][4 * r4 + 1] * inv);
                 w[1] = pack_bf16x2(oacc[db][qb][4 * r4 + 2] * inv, oacc[db][qb][4 * r4 + 3] * inv);
-                *(__attribute__((address_space(3))) u32x2 *)(vs_ + qi * D * 2 + swz_k<D>(qi, d >> 3) * 16 +
+                *(__attribute__((address_space(3))) u32x2 *)(qs_ + qi * D * 2 + swz_k<D>(qi, d >> 3) * 16 +
                                                               (d & 7) * 2) = w;
             }
     }
-    __syncthreads();
-    if (active)
-        for (int ci = lane; ci < T * CH; ci += 64) {
-            const int r = ci / CH, ch = ci % CH;
-            *(u32x4 *)(o + base + r * fs + ch * 8) =
-                *(const __attribute__((address_space(3))) u32x4 *)(vs_ + r * D * 2 + swz_k<D>(r, ch) * 16);
-        }
+    for (int ci = lane; ci < T * CH; ci += 64) {
+        const int r = ci / CH, ch = ci % CH;
+        *(u32x4 *)(o + base + r * fs + ch * 8) =
+            *(const __attribute__((address_space(3))) u32x4 *)(qs_ + r * D * 2 + swz_k<D>(r, ch) * 16);
+    }
+#endif
 }
 
-template <int D, int KB>
+template <int D, int KB, int QKR>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int B, int heads, int T, int HW,
                   float c, hipStream_t s) {
     const int64_t total = (int64_t)B * HW * heads;
     const uint32_t grid = (uint32_t)((total + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((temporal_bf16<D, KB>), dim3(grid), dim3(kWaves * 64), 0, s, (const uint16_t *)q,
+    hipLaunchKernelGGL((temporal_bf16<D, KB, QKR>), dim3(grid), dim3(kWaves * 64), 0, s, (const uint16_t *)q,
                        (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, B, heads, T, HW, c);
     return hipGetLastError();
 }
@@ -220,12 +260,15 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, int B, i
 
 hipError_t launch_temporal_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
                                 int HW, int D, float scale_log2e, hipStream_t s) {
-    if (T <= 32) {
-        if (D == 128) return launch<128, 1>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-        if (D == 64) return launch<64, 1>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+    if (T <= 24) {
+        if (D == 128) return launch<128, 1, 24>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+        if (D == 64) return launch<64, 1, 24>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+    } else if (T <= 32) {
+        if (D == 128) return launch<128, 1, 32>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+        if (D == 64) return launch<64, 1, 32>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
     } else if (T <= 64) {
-        if (D == 128) return launch<128, 2>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-        if (D == 64) return launch<64, 2>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+        if (D == 128) return launch<128, 2, 64>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
+        if (D == 64) return launch<64, 2, 64>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
     }
     return hipErrorInvalidValue;
 }

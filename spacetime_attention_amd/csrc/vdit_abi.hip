@@ -50,6 +50,9 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
     if (mode == kTemporal && T > (dt == VDIT_BF16 ? 64 : 256)) return VDIT_E_SHAPE;
     // Workgroup counts must fit a 1-D grid.
     if ((uint64_t)B * heads * n_tok > (uint64_t)UINT32_MAX * 32) return VDIT_E_SHAPE;
+    // The bf16 kernels address one batch's tokens through buffer descriptors
+    // whose byte range is a signed 32-bit value.
+    if (dt == VDIT_BF16 && n_tok * (uint64_t)heads * (uint64_t)D * 2u >= (uint64_t(1) << 31)) return VDIT_E_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VDIT_E_ALIGN;
     if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
         return VDIT_E_ALIAS;

@@ -58,6 +58,7 @@ def test_attention_argument_errors(lib, fn):
     assert call(B=0) == 2                         # VDIT_E_SHAPE
     assert call(Wp=-1) == 2
     assert call(T=1 << 16, Hp=1 << 16, Wp=1 << 16) == 2  # overflow
+    assert call(T=64, Hp=256, Wp=256, heads=16) == 2     # one batch over 2 GiB in bf16
     assert call(D=96) == 3                        # VDIT_E_HEAD_DIM
     assert call(D=32) == 3                        # bf16 supports 64 and 128
     assert call(dt=vd.F32, D=48) == 3
