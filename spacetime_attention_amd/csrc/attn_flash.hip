@@ -217,21 +217,47 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     auto tile = [&](auto bufc, int j) {
         constexpr int BUF = decltype(bufc)::value;
         constexpr uint32_t B0 = BUF * 2 * S::TILE;
+        constexpr int RB = D * 2;  // bytes per row
+        // LDS operand reads run one step ahead of the MFMAs that use them,
+        // in a second set of registers; scheduling fences keep the compiler
+        // from sinking them back to their uses.
+        bf16x8 ka[2][2];
+        auto rdk = [&](int ks, int slot) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                ka[slot][kb2] = *(const __attribute__((address_space(3))) bf16x8 *)(
+                    lds + kofs[ks] + (B0 + kb2 * 32 * RB));
+        };
+        bf16x4 va[2][S::DB][2];
+        auto rdv = [&](int st, int slot) {
+            const uint32_t off = B0 + S::TILE + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
+#pragma unroll
+            for (int db = 0; db < S::DB; ++db) {
+                va[slot][db][0] = lds_read_tr(lds + (vofs[db] - S::TILE) + off);
+                va[slot][db][1] = lds_read_tr(lds + (vofs[db] - S::TILE) + (off + 8 * RB));
+            }
+        };
+
+        // S^T = K Q^T for both 32-key blocks.
         f32x16 sacc[2][QB];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb] = (f32x16){};
+        rdk(0, 0);
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
+        for (int ks = 0; ks < S::KS; ++ks) {
+            if (ks + 1 < S::KS) rdk(ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-                    lds + kofs[ks] + (B0 + kb2 * 32 * D * 2));
+            for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
-            }
+                    sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb2], qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
+        }
+        // The first 16-key step's V operands load under the softmax.
+        rdv(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 
         // Keys past the end of the segment (last tile only).
         const int kvalid = L - j * kBN;
@@ -290,20 +316,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
         // O^T += V^T P^T over the tile's four 16-key steps.
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int st = 0; st < 4; ++st) {
+            if (st + 1 < 4) rdv(st + 1, (st + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+            for (int db = 0; db < S::DB; ++db) {
+                const bf16x8 a = __builtin_shufflevector(va[st & 1][db][0], va[st & 1][db][1], 0, 1, 2, 3, 4,
+                                                         5, 6, 7);
 #pragma unroll
-                for (int db = 0; db < S::DB; ++db) {
-                    constexpr int RB = D * 2;  // bytes per row
-                    const uint32_t off = B0 + (kb2 * 32 + 16 * s2) * RB;
-                    const bf16x4 lo = lds_read_tr(lds + vofs[db] + off);
-                    const bf16x4 hi = lds_read_tr(lds + vofs[db] + (off + 8 * RB));
-                    const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][kb2][s2], oacc[db][qb], 0, 0, 0);
-                }
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][st >> 1][st & 1], oacc[db][qb], 0, 0, 0);
+            }
+        }
     };
 
     load_tile(0, 0);
