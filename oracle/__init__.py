@@ -68,6 +68,10 @@ def _load():
                                                                       ctypes.POINTER(ctypes.c_int64),
                                                                       ctypes.c_int64]
         lib.oracle_attention.restype = i
+        lib.oracle_cross_attention.argtypes = [dp, dp, dp, dp] + [i] * 5 + [ctypes.c_double,
+                                                                            ctypes.POINTER(ctypes.c_int64),
+                                                                            ctypes.c_int64]
+        lib.oracle_cross_attention.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -149,6 +153,27 @@ def attention(q, k, v, grid: Tuple[int, int, int], mode: str = "full",
     out = np.empty((B, nrows, heads, D), dtype=np.float64)
     _check(_load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, Hp, Wp,
                                     heads, D, float(scale), _MODES[mode], rp, nrows))
+    return out
+
+
+def cross_attention(q, k, v, scale: float = 0.0, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Cross-attention, q: (B, Nq, heads, D), k/v: (B, Nk, heads, D).
+
+    With ``rows`` (query tokens), returns (B, len(rows), heads, D).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Nq, heads, D = q.shape
+    Bk, Nk, hk, Dk = k.shape
+    if (Bk, hk, Dk) != (B, heads, D) or v.shape != k.shape:
+        raise OracleError("q and k/v shapes do not match")
+    if rows is None:
+        rp, nrows = None, Nq
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rp, nrows = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(rows.size)
+    out = np.empty((B, nrows, heads, D), dtype=np.float64)
+    _check(_load().oracle_cross_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Nq, Nk, heads, D,
+                                          float(scale), rp, nrows))
     return out
 
 

@@ -232,6 +232,82 @@ int oracle_attention(const double *q, const double *k, const double *v, double *
     return failed ? ORACLE_E_NOMEM : ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Cross-attention: queries of one token set attend to all keys of another.
+ *
+ * "How AI Generates Video ...", section 5, attn2: the video tokens supply the
+ * queries and the text-prompt tokens (512 UMT5 embeddings, projected to the
+ * model width) supply the keys and values; "Video Diffusion Models, in
+ * depth", Step 3, likewise has the video tokens read the text embeddings.
+ *   l_m = scale * <q_n, k_m>  for m = 0..Nk-1
+ *   o_n = sum_m exp(l_m - M) v_m / sum_m exp(l_m - M),  M = max_m l_m
+ * q, o: [B][Nq][heads][D]; k, v: [B][Nk][heads][D]. rows as in
+ * oracle_attention (a list of nrows query tokens, or NULL for all Nq).
+ * ------------------------------------------------------------------------ */
+int oracle_cross_attention(const double *q, const double *k, const double *v, double *o,
+                           int B, int Nq, int Nk, int heads, int D, double scale,
+                           const int64_t *rows, int64_t nrows)
+{
+    if (!q || !k || !v || !o || B <= 0 || Nq <= 0 || Nk <= 0 || heads <= 0 || D <= 0)
+        return ORACLE_E_ARG;
+    if (rows == NULL && nrows != Nq)
+        return ORACLE_E_ARG;
+    if (nrows <= 0)
+        return ORACLE_E_ARG;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= Nq)
+                return ORACLE_E_ARG;
+    if (scale <= 0.0)
+        scale = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)Nk);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!logit || !acc) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for schedule(dynamic, 4) collapse(3)
+        for (int b = 0; b < B; ++b)
+            for (int hd = 0; hd < heads; ++hd)
+                for (int64_t r = 0; r < nrows; ++r) {
+                    if (!logit || !acc)
+                        continue;
+                    const int64_t n = rows ? rows[r] : r;
+                    const double *qn = q + (((int64_t)b * Nq + n) * heads + hd) * D;
+                    double M = -INFINITY;
+                    for (int m = 0; m < Nk; ++m) {
+                        const double *km = k + (((int64_t)b * Nk + m) * heads + hd) * D;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            dot += qn[d] * km[d];
+                        logit[m] = scale * dot;
+                        if (logit[m] > M)
+                            M = logit[m];
+                    }
+                    double sum = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        acc[d] = 0.0;
+                    for (int m = 0; m < Nk; ++m) {
+                        const double wgt = exp(logit[m] - M);
+                        const double *vm = v + (((int64_t)b * Nk + m) * heads + hd) * D;
+                        sum += wgt;
+                        for (int d = 0; d < D; ++d)
+                            acc[d] += wgt * vm[d];
+                    }
+                    double *on = o + (((int64_t)b * nrows + r) * heads + hd) * D;
+                    for (int d = 0; d < D; ++d)
+                        on[d] = acc[d] / sum;
+                }
+        free(logit);
+        free(acc);
+    }
+    return failed ? ORACLE_E_NOMEM : ORACLE_OK;
+}
+
 /* Number of threads OpenMP will use for the routines above. */
 int oracle_num_threads(void)
 {

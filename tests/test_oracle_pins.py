@@ -327,3 +327,35 @@ def test_rope_bad_split_raises(split):
         return
     with pytest.raises(oracle.RopeSplitError):
         oracle.rope3d(x, (1, 2, 3), split)
+
+
+# ----------------------------------------------------------------------------
+# Cross-attention (video queries against text keys)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Nq,Nk,D", [(7, 5, 32), (40, 64, 128), (33, 1, 64)])
+def test_cross_matches_sdpa(Nq, Nk, D):
+    q = RNG.standard_normal((2, Nq, 3, D))
+    k = RNG.standard_normal((2, Nk, 3, D))
+    v = RNG.standard_normal((2, Nk, 3, D))
+    np.testing.assert_allclose(oracle.cross_attention(q, k, v), _sdpa(q, k, v), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.cross_attention(q, k, v, scale=0.7), _sdpa(q, k, v, scale=0.7),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_cross_closed_forms():
+    q = RNG.standard_normal((1, 9, 2, 16))
+    k = RNG.standard_normal((1, 6, 2, 16))
+    v = RNG.standard_normal((1, 6, 2, 16))
+    # One key: every query returns it exactly.
+    np.testing.assert_array_equal(oracle.cross_attention(q, k[:, :1], v[:, :1]),
+                                  np.broadcast_to(v[:, :1], q.shape))
+    # Zero queries: the mean of the values.
+    np.testing.assert_allclose(oracle.cross_attention(np.zeros_like(q), k, v),
+                               np.broadcast_to(v.mean(axis=1, keepdims=True), q.shape), rtol=1e-12, atol=1e-14)
+    # Same keys as the queries' own token set: cross equals full attention.
+    x = RNG.standard_normal((1, 12, 2, 16))
+    np.testing.assert_allclose(oracle.cross_attention(x, x, x), oracle.attention(x, x, x, (1, 3, 4), "full"),
+                               rtol=1e-13, atol=1e-14)
+    rows = np.array([0, 5, 8], dtype=np.int64)
+    np.testing.assert_array_equal(oracle.cross_attention(q, k, v, rows=rows), oracle.cross_attention(q, k, v)[:, rows])
