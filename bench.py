@@ -213,9 +213,33 @@ def main():
         "cpu_baseline": None,
     }
 
+    result["next_rows"] = {"cross": bench_cross(vd, torch)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
     print(json.dumps(result), flush=True)
+
+
+def bench_cross(vd, torch, iters: int = 20):
+    """Cross-attention (the block's attn2), timed on its own after the step:
+    32,760 video queries x 512 text keys, 12 heads x 128, bf16."""
+    from synthetic_inputs import CROSS_WORKLOADS
+    w = CROSS_WORKLOADS["cross_480p"]
+    d = w.draw()
+    q, k, v = (_dev(d[n]) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    for _ in range(3):
+        vd.attn_cross(q, k, v, out=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        vd.attn_cross(q, k, v, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    flop = 4.0 * w.B * w.heads * w.Nq * w.Nk * w.head_dim
+    return {"workload": f"q [{w.B},{w.Nq},{w.heads},{w.head_dim}] x k/v [{w.B},{w.Nk},{w.heads},{w.head_dim}]",
+            "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 
 def cpu_baseline(df, wf):

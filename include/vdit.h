@@ -11,7 +11,9 @@
  *   vdit_attn_spatial   the same, with keys limited to the query's own latent
  *                       frame;
  *   vdit_attn_temporal  the same, with keys limited to the query's own patch
- *                       position across frames.
+ *                       position across frames;
+ *   vdit_attn_cross     attention from the video tokens to another token set
+ *                       (the text prompt).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -170,6 +172,26 @@ vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, voi
 vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, void *o,
                                  int B, int heads, int T, int Hp, int Wp, int head_dim,
                                  float scale, vdit_dtype_t dtype, void *stream);
+
+/*
+ * vdit_attn_cross — cross-attention from the video tokens to another token
+ * set (the text prompt).
+ *
+ * "How AI Generates Video ...", section 5 (attn2: the video bricks supply the
+ * queries, the 512 UMT5 text embeddings, projected to the model width, the
+ * keys and values); "Video Diffusion Models, in depth", Step 3 (the video
+ * tokens read the text embeddings):
+ *   o[b][n][h] = sum_m softmax_m(scale * <q[b][n][h], k[b][m][h]>) v[b][m][h],
+ * m over all Nk keys of batch b, no mask. 4*Nq*Nk*head_dim FLOP per (b, head).
+ *
+ * q, o : [B, Nq, heads, head_dim]; k, v : [B, Nk, heads, head_dim], token-
+ *        major. o may not overlap q, k or v (VDIT_E_ALIAS).
+ * scale, head_dim, dtype and the 2 GiB-per-batch bf16 limit (on both token
+ * sets) as vdit_attn_full.
+ */
+vdit_status_t vdit_attn_cross(const void *q, const void *k, const void *v, void *o,
+                              int B, int heads, int Nq, int Nk, int head_dim,
+                              float scale, vdit_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,7 @@ Functions (names as in the C ABI, without the ``vdit_`` prefix):
   attn_full(q, k, v, grid, scale=0.0, out=None)
   attn_spatial(q, k, v, grid, scale=0.0, out=None)
   attn_temporal(q, k, v, grid, scale=0.0, out=None)
+  attn_cross(q, k, v, scale=0.0, out=None)
 Token tensors are ``[B, N, heads, head_dim]`` with ``N = T*Hp*Wp`` and token
 ``(t, h, w)`` at ``n = (t*Hp + h)*Wp + w``; ``grid = (T, Hp, Wp)``.
 """
@@ -33,7 +34,7 @@ BF16, F32 = 0, 1
 STATUS = ["VDIT_OK", "VDIT_E_NULL", "VDIT_E_SHAPE", "VDIT_E_HEAD_DIM", "VDIT_E_ROPE_SPLIT",
           "VDIT_E_ALIGN", "VDIT_E_ALIAS", "VDIT_E_DTYPE", "VDIT_E_LAUNCH"]
 EXPORTS = ("vdit_status_str", "vdit_patchify", "vdit_rope3d", "vdit_attn_full",
-           "vdit_attn_spatial", "vdit_attn_temporal")
+           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross")
 
 
 class VditError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp] + [i] * 6 + [f, i, vp]
         fn.restype = i
+    lib.vdit_attn_cross.argtypes = [vp, vp, vp, vp] + [i] * 5 + [f, i, vp]
+    lib.vdit_attn_cross.restype = i
     _lib = lib
     return lib
 
@@ -175,6 +178,24 @@ def attn_spatial(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:
 def attn_temporal(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:
     """Attention across frames at each patch position."""
     return _attn("vdit_attn_temporal", q, k, v, grid, scale, out)
+
+
+def attn_cross(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float = 0.0,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Cross-attention: q ``[B, Nq, heads, D]`` against k/v ``[B, Nk, heads, D]``."""
+    B, Nq, heads, D = q.shape
+    Bk, Nk, hk, Dk = k.shape
+    if (Bk, hk, Dk) != (B, heads, D) or v.shape != k.shape:
+        raise ValueError("q and k/v shapes do not match")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out has the wrong shape")
+    lib = load_library()
+    dt = q.dtype
+    _check(lib.vdit_attn_cross(_dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
+                               B, heads, Nq, Nk, D, float(scale), _dtype_code(q), _stream(q)))
+    return out
 
 
 def divided(x: torch.Tensor, grid, order=("spatial", "temporal"), split: Optional[Sequence[int]] = None,

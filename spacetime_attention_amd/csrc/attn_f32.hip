@@ -113,6 +113,74 @@ __global__ __launch_bounds__(kQ) void attn_f32_kernel(const float *__restrict__ 
     }
 }
 
+// Cross-attention in fp32: one thread per (b, query, head); the Nk keys of
+// batch b are staged through LDS in tiles shared by the workgroup's queries.
+template <int D>
+__global__ __launch_bounds__(kQ) void cross_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                       const float *__restrict__ v, float *__restrict__ o, int B,
+                                                       int heads, int Nq, int Nk, float scale)
+{
+    __shared__ float ks[kTile][D];
+    __shared__ float vs[kTile][D];
+    const int64_t groups = (Nq + kQ - 1) / kQ;
+    const int64_t gi = blockIdx.x % groups;
+    const int hd = (int)((blockIdx.x / groups) % heads);
+    const int b = (int)(blockIdx.x / (groups * heads));
+    const int64_t n = gi * kQ + threadIdx.x;
+    const bool valid = n < Nq;
+
+    float qr[D], acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = valid ? q[(((int64_t)b * Nq + n) * heads + hd) * D + d] : 0.f;
+        acc[d] = 0.f;
+    }
+    float mx = -INFINITY, l = 0.f;
+    for (int m0 = 0; m0 < Nk; m0 += kTile) {
+        const int nk = (Nk - m0) < kTile ? (Nk - m0) : kTile;
+        for (int i = threadIdx.x; i < nk * D; i += kQ) {
+            const int r = i / D, d = i % D;
+            const int64_t key = (int64_t)b * Nk + m0 + r;
+            ks[r][d] = k[(key * heads + hd) * D + d];
+            vs[r][d] = v[(key * heads + hd) * D + d];
+        }
+        __syncthreads();
+        if (valid)
+            for (int r = 0; r < nk; ++r) {
+                float sc = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) sc = fmaf(qr[d], ks[r][d], sc);
+                sc *= scale;
+                if (sc > mx) {
+                    const float corr = expf(mx - sc);
+                    l *= corr;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) acc[d] *= corr;
+                    mx = sc;
+                }
+                const float p = expf(sc - mx);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[r][d], acc[d]);
+            }
+        __syncthreads();
+    }
+    if (valid) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int d = 0; d < D; ++d) o[(((int64_t)b * Nq + n) * heads + hd) * D + d] = acc[d] * inv;
+    }
+}
+
+template <int D>
+hipError_t launch_cross(const float *q, const float *k, const float *v, float *o, int B, int heads, int Nq,
+                        int Nk, float scale, hipStream_t s) {
+    const int64_t groups = (int64_t)((Nq + kQ - 1) / kQ) * heads * B;
+    hipLaunchKernelGGL(cross_f32_kernel<D>, dim3((uint32_t)groups), dim3(kQ), 0, s, q, k, v, o, B, heads, Nq, Nk,
+                       scale);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch(const float *q, const float *k, const float *v, float *o, int B, int heads, int T,
                   int HW, int mode, float scale, hipStream_t s) {
@@ -125,6 +193,16 @@ hipError_t launch(const float *q, const float *k, const float *v, float *o, int 
 }
 
 }  // namespace
+
+hipError_t launch_cross_f32(const float *q, const float *k, const float *v, float *o, int B, int heads, int Nq,
+                            int Nk, int D, float scale, hipStream_t s) {
+    switch (D) {
+        case 32: return launch_cross<32>(q, k, v, o, B, heads, Nq, Nk, scale, s);
+        case 64: return launch_cross<64>(q, k, v, o, B, heads, Nq, Nk, scale, s);
+        case 128: return launch_cross<128>(q, k, v, o, B, heads, Nq, Nk, scale, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, int B, int heads,
                            int T, int HW, int D, int mode, float scale, hipStream_t s) {

@@ -3,9 +3,11 @@
 // Computes o = softmax(scale * q k^T) v per (segment, head) without forming
 // the score matrix: the tiled form that "Video Diffusion Models, in depth"
 // (Step 3) calls mandatory, with an online softmax in fp32 (its "Failure
-// modes" keep softmax in FP32). A segment is a run of L consecutive tokens
-// whose queries see exactly its keys: the whole clip for full 3D attention,
-// one latent frame (Hp*Wp tokens) for the spatial pass.
+// modes" keep softmax in FP32). A segment is a run of L consecutive query
+// tokens whose keys are the segment's Lk consecutive key tokens: the whole
+// clip for full 3D attention, one latent frame (Hp*Wp tokens) for the
+// spatial pass (Lk = L for both), and the whole text prompt for
+// cross-attention ("How AI Generates Video ...", section 5, attn2).
 //
 // Layout of the work (one workgroup = 4 wavefronts = BM query tokens):
 //  * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
@@ -104,12 +106,14 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// PASS (0 full, 1 spatial) only names the instantiation, so that profiles
-// attribute the two passes separately; the code is the same.
+// PASS (0 full, 1 spatial, 2 cross) only names the instantiation, so that
+// profiles attribute the passes separately; the code is the same. L is the
+// number of queries and Lk the number of keys per segment (equal for self-
+// attention; the text length for cross-attention).
 template <int D, int QB, int NW, int PASS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    uint16_t *__restrict__ o, int nseg, int L, int heads, float c)
+    uint16_t *__restrict__ o, int nseg, int L, int Lk, int heads, float c)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using S = FlashShape<D, QB, NW>;
@@ -127,8 +131,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int half = lane >> 5, col = lane & 31;
     const int64_t rs = (int64_t)heads * D;  // elements between consecutive tokens
-    const int64_t base = ((int64_t)seg * L * heads + hd) * D;
-    const uint16_t *qp = q + base, *kp = k + base, *vp = v + base;
+    const int64_t base = ((int64_t)seg * L * heads + hd) * D;     // query / output rows
+    const int64_t kvbase = ((int64_t)seg * Lk * heads + hd) * D;  // key / value rows
+    const uint16_t *qp = q + base, *kp = k + kvbase, *vp = v + kvbase;
     uint16_t *op = o + base;
 
     // This wave's queries, as B operands of S^T = K Q^T.
@@ -147,8 +152,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     }
 
     // Buffer descriptors over this (segment, head)'s keys and values: the
-    // size stops at the end of key L-1's row, so any row >= L reads as zero.
-    const int nrec = (int)(((int64_t)(L - 1) * rs + D) * 2);
+    // size stops at the end of key Lk-1's row, so any row >= Lk reads as zero.
+    const int nrec = (int)(((int64_t)(Lk - 1) * rs + D) * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kp, 0, nrec, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vp, 0, nrec, kBufferFlags);
     // Per-lane byte offsets (within a tile) of the chunks this lane fetches:
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         lsum[qb] = 0.f;
     }
 
-    const int ntiles = (L + kBN - 1) / kBN;
+    const int ntiles = (Lk + kBN - 1) / kBN;
 
     // One 64-key tile held in LDS buffer BUF: S^T for both 32-key blocks,
     // the online softmax over the tile, then O^T += V^T P^T.
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         __builtin_amdgcn_sched_barrier(0);
 
         // Keys past the end of the segment (last tile only).
-        const int kvalid = L - j * kBN;
+        const int kvalid = Lk - j * kBN;
         if (kvalid < kBN) {
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -372,27 +377,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 }
 
 template <int D, int QB, int NW, int PASS>
-hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int heads,
-                  float c, hipStream_t s) {
+hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
+                  int heads, float c, hipStream_t s) {
     using S = FlashShape<D, QB, NW>;
     const int nqb = (L + S::BM - 1) / S::BM;
     const uint32_t grid = (uint32_t)nseg * heads * nqb;
     hipLaunchKernelGGL((flash_fwd_bf16<D, QB, NW, PASS>), dim3(grid), dim3(S::THREADS), 0, s,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
-                       nseg, L, heads, c);
+                       nseg, L, Lk, heads, c);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L,
-                             int heads, int D, float scale_log2e, bool spatial, hipStream_t s) {
-    if (D == 128)
-        return spatial ? launch<128, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
-                       : launch<128, 1, kFullWaves, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
-    if (D == 64)
-        return spatial ? launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, heads, scale_log2e, s)
-                       : launch<64, 1, kFullWaves, 0>(q, k, v, o, nseg, L, heads, scale_log2e, s);
+                             int Lk, int heads, int D, float scale_log2e, int pass, hipStream_t s) {
+    if (D == 128) {
+        if (pass == 0) return launch<128, 1, kFullWaves, 0>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        if (pass == 1) return launch<128, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        return launch<128, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+    }
+    if (D == 64) {
+        if (pass == 0) return launch<64, 1, kFullWaves, 0>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        if (pass == 1) return launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        return launch<64, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+    }
     return hipErrorInvalidValue;
 }
 

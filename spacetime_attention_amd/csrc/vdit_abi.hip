@@ -65,8 +65,8 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
                                              heads, T, HW, D, (int)mode, s, st));
     const float c = (float)((double)s * kLog2e);
     switch (mode) {
-        case kFull: return launch_status(launch_flash_bf16(q, k, v, o, B, T * HW, heads, D, c, false, st));
-        case kSpatial: return launch_status(launch_flash_bf16(q, k, v, o, B * T, HW, heads, D, c, true, st));
+        case kFull: return launch_status(launch_flash_bf16(q, k, v, o, B, T * HW, T * HW, heads, D, c, 0, st));
+        case kSpatial: return launch_status(launch_flash_bf16(q, k, v, o, B * T, HW, HW, heads, D, c, 1, st));
         default: return launch_status(launch_temporal_bf16(q, k, v, o, B, heads, T, HW, D, c, st));
     }
 }
@@ -103,6 +103,33 @@ vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, voi
 vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
                                  int Hp, int Wp, int head_dim, float scale, vdit_dtype_t dtype, void *stream) {
     return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kTemporal);
+}
+
+vdit_status_t vdit_attn_cross(const void *q, const void *k, const void *v, void *o, int B, int heads, int Nq,
+                              int Nk, int head_dim, float scale, vdit_dtype_t dtype, void *stream) {
+    if (!q || !k || !v || !o) return VDIT_E_NULL;
+    if (dtype != VDIT_BF16 && dtype != VDIT_F32) return VDIT_E_DTYPE;
+    if (B <= 0 || heads <= 0 || Nq <= 0 || Nk <= 0 || head_dim <= 0) return VDIT_E_SHAPE;
+    const int D = head_dim;
+    if (dtype == VDIT_BF16 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    if (dtype == VDIT_F32 && D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    uint64_t qe = 1, ke = 1;
+    if (!mul_ok(qe, B) || !mul_ok(qe, Nq) || !mul_ok(qe, heads) || !mul_ok(qe, D)) return VDIT_E_SHAPE;
+    if (!mul_ok(ke, B) || !mul_ok(ke, Nk) || !mul_ok(ke, heads) || !mul_ok(ke, D)) return VDIT_E_SHAPE;
+    if ((uint64_t)B * heads * (uint64_t)Nq > (uint64_t)UINT32_MAX * 32) return VDIT_E_SHAPE;
+    if (dtype == VDIT_BF16 && ((uint64_t)Nk * heads * D * 2u >= (uint64_t(1) << 31) ||
+                               (uint64_t)Nq * heads * D * 2u >= (uint64_t(1) << 31)))
+        return VDIT_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VDIT_E_ALIGN;
+    const uint64_t es = (uint64_t)esize(dtype);
+    if (overlap(o, qe * es, q, qe * es) || overlap(o, qe * es, k, ke * es) || overlap(o, qe * es, v, ke * es))
+        return VDIT_E_ALIAS;
+    const float s = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == VDIT_F32)
+        return launch_status(launch_cross_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, B,
+                                              heads, Nq, Nk, D, s, st));
+    return launch_status(launch_flash_bf16(q, k, v, o, B, Nq, Nk, heads, D, (float)((double)s * kLog2e), 2, st));
 }
 
 vdit_status_t vdit_patchify(const void *latent, const void *weight, const void *bias, void *tokens, int B, int C,

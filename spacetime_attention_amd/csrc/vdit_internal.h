@@ -41,12 +41,15 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t hw_id, uint32_t tota
 
 // ---- launchers (each returns hipGetLastError() after its launch) ----------
 
-// Softmax attention over contiguous segments: nseg segments of L tokens each
-// (segment s covers rows [s*L, (s+1)*L) of the [nseg*L, heads, D] arrays);
-// queries of a segment attend to the keys of the same segment. Full attention
-// is nseg = B, L = N; the spatial pass is nseg = B*T, L = Hp*Wp.
+// Softmax attention over contiguous segments: segment s has L query rows
+// [s*L, (s+1)*L) of q/o and Lk key rows [s*Lk, (s+1)*Lk) of k/v, all arrays
+// [rows, heads, D]; its queries attend to exactly its keys. Full attention is
+// nseg = B, L = Lk = N; the spatial pass nseg = B*T, L = Lk = Hp*Wp;
+// cross-attention nseg = B, L = Nq, Lk = Nk. pass: 0 full, 1 spatial,
+// 2 cross (selects the tuned instantiation).
 hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *o, int nseg,
-                             int L, int heads, int D, float scale_log2e, bool spatial, hipStream_t s);
+                             int L, int Lk, int heads, int D, float scale_log2e, int pass,
+                             hipStream_t s);
 
 // fp32 attention with a generic key set: query token n of batch b has keys
 // key(m) = kbase(n) + m*kstride, m < nkeys, where for mode 0 (full)
@@ -55,6 +58,9 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
 // nkeys = T.
 hipError_t launch_attn_f32(const float *q, const float *k, const float *v, float *o, int B,
                            int heads, int T, int HW, int D, int mode, float scale, hipStream_t s);
+// fp32 cross-attention: q/o [B, Nq, heads, D], k/v [B, Nk, heads, D].
+hipError_t launch_cross_f32(const float *q, const float *k, const float *v, float *o, int B,
+                            int heads, int Nq, int Nk, int D, float scale, hipStream_t s);
 
 // Temporal pass in bf16: one wavefront per (b, position, head) sequence of T
 // tokens at stride HW tokens.

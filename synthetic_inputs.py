@@ -186,6 +186,33 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class CrossWorkload:
+    """Video queries ``[B, Nq, heads, head_dim]`` against text keys and values
+    ``[B, Nk, heads, head_dim]``, drawn N(0,1) in the order q, k, v."""
+    name: str
+    B: int
+    Nq: int
+    Nk: int
+    heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+
+    def draw(self, q_scale: float = 1.0) -> Dict[str, Drawn]:
+        qs = (self.B, self.Nq, self.heads, self.head_dim)
+        ks = (self.B, self.Nk, self.heads, self.head_dim)
+        return draw(self.seed, [("q", qs, q_scale), ("k", ks, q_scale), ("v", ks, 1.0)], self.dtype)
+
+
+CROSS_WORKLOADS: Dict[str, CrossWorkload] = {
+    # Wan 1.3B attn2 at 480p / 81 frames: 32,760 video queries against the 512
+    # UMT5 text embeddings projected to 12 heads x 128.
+    "cross_480p": CrossWorkload("cross_480p", B=1, Nq=32760, Nk=512, heads=12, head_dim=128,
+                                dtype="bf16", seed=5),
+}
+
+
 def small_grid(name: str, B: int, T: int, Hp: int, Wp: int, heads: int, head_dim: int,
                dtype: str, seed: int, **kw) -> Workload:
     """An ad-hoc workload for parity and edge cases."""

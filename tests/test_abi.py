@@ -98,3 +98,18 @@ def test_patchify_argument_errors(lib):
     assert call(heads=1, D=12) == 2               # output width not a multiple of 8
     assert call(o=Q + 16) == 6
     assert call(w=K + 4) == 5
+
+
+def test_cross_argument_errors(lib):
+    f = lib.vdit_attn_cross
+
+    def call(q=Q, k=K, v=V, o=O, B=1, heads=2, Nq=100, Nk=20, D=128, scale=0.0, dt=vd.BF16):
+        return f(q, k, v, o, B, heads, Nq, Nk, D, scale, dt, None)
+
+    assert call(k=None) == 1
+    assert call(Nk=0) == 2
+    assert call(Nq=-3) == 2
+    assert call(D=48) == 3
+    assert call(v=V + 8) == 5
+    assert call(o=K + 16) == 6                    # o overlaps k
+    assert call(dt=9) == 7

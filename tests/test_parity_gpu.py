@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import spacetime_attention_amd as vd
-from synthetic_inputs import WORKLOADS, draw, sample_rows, small_grid
+from synthetic_inputs import CROSS_WORKLOADS, WORKLOADS, CrossWorkload, draw, sample_rows, small_grid
 from tests.parity_util import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -250,3 +250,56 @@ def test_block_input_path():
     got_x2 = to_host(x2[:, torch.from_numpy(rows).cuda()])
     assert_close(to_host(x1[:, torch.from_numpy(rows).cuda()]), sp_rows, "bf16", "block/spatial")
     assert_close(got_x2, ref_x2, "bf16", "block/spatial-then-temporal")
+
+
+# ----------------------------------------------------------------------------
+# Cross-attention (video queries, text keys)
+# ----------------------------------------------------------------------------
+
+CROSS_SMALL = [("cross_231x77", 2, 231, 77, 2, 128), ("cross_1000x512", 1, 1000, 512, 2, 128),
+               ("cross_d64", 1, 300, 130, 3, 64), ("cross_one_key", 2, 150, 1, 2, 128)]
+
+
+@pytest.mark.parametrize("case", CROSS_SMALL, ids=[c[0] for c in CROSS_SMALL])
+def test_cross_small_bf16(case):
+    name, B, Nq, Nk, heads, D = case
+    _announce(f"cross bf16 {name}")
+    w = CrossWorkload(name, B, Nq, Nk, heads, D, "bf16", seed=60 + Nk)
+    d = w.draw()
+    q, k, v = (to_dev(d[n]) for n in ("q", "k", "v"))
+    got = vd.attn_cross(q, k, v)
+    if Nk == 1:  # a single key: every query returns it bit for bit
+        assert torch.equal(got, v.expand_as(got))
+        return
+    ref = oracle.cross_attention(d["q"].f32, d["k"].f32, d["v"].f32)
+    assert_close(to_host(got), ref, "bf16", f"{name}")
+
+
+def test_cross_peaky_bf16():
+    _announce("cross peaky")
+    w = CrossWorkload("cross_peaky", 1, 400, 200, 2, 128, "bf16", seed=77)
+    d = w.draw(q_scale=4.0)
+    q, k, v = (to_dev(d[n]) for n in ("q", "k", "v"))
+    ref = oracle.cross_attention(d["q"].f32, d["k"].f32, d["v"].f32)
+    assert_close(to_host(vd.attn_cross(q, k, v)), ref, "bf16", "cross/peaky")
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_cross_f32(D):
+    _announce(f"cross f32 D={D}")
+    w = CrossWorkload("cross_f32", 2, 70, 45, 2, D, "f32", seed=78)
+    d = w.draw()
+    q, k, v = (to_dev(d[n]) for n in ("q", "k", "v"))
+    ref = oracle.cross_attention(d["q"].f32, d["k"].f32, d["v"].f32)
+    assert_close(to_host(vd.attn_cross(q, k, v)), ref, "f32", f"cross/f32/D{D}")
+
+
+def test_cross_480p_sampled():
+    w = CROSS_WORKLOADS["cross_480p"]
+    _announce("cross 480p: 32,760 video queries x 512 text keys, rows every 127")
+    d = w.draw()
+    q, k, v = (to_dev(d[n]) for n in ("q", "k", "v"))
+    got = vd.attn_cross(q, k, v)
+    rows = sample_rows(w.Nq, 127, offset=3)
+    ref = oracle.cross_attention(d["q"].f32, d["k"].f32, d["v"].f32, rows=rows)
+    assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", "cross_480p")
