@@ -11,12 +11,13 @@
 // row-major matrix. Output rows are token-major, m = b*N + (t*Hp+h)*Wp + w.
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation): a workgroup owns
-// 64 tokens; it gathers their [64][K] patch matrix into LDS once and sweeps
-// all output channels in chunks of 128, each wave computing a 32-channel x
-// 64-token block of C^T = W A^T with W read straight from global (it is small
-// and stays in L2). Each output chunk is staged through LDS and written as
-// whole 256-byte row runs: at K = 64 the kernel writes 24x more bytes than it
-// reads, so coalesced stores set its speed.
+// kTok tokens; it gathers their [kTok][K] patch matrix into LDS once and
+// sweeps all output channels in chunks of 128, each wave computing a
+// 32-channel x kTok-token block of C^T = W A^T with W read straight from
+// global (it is small and stays in L2). Each chunk is staged through LDS and
+// written as whole 256-byte row runs: at K = 64 the kernel writes 24x more
+// bytes than it reads, so coalesced stores set its speed. LDS is sized to the
+// actual patch length so several workgroups share a CU.
 //
 // fp32 path: one thread per output element, a plain dot product (for the
 // small fp32 workloads that must agree with fp64 to 1e-5).
@@ -25,26 +26,32 @@
 namespace vdit {
 namespace {
 
-constexpr int kTok = 64;   // tokens per workgroup
+constexpr int kTok = 32;   // tokens per workgroup
+constexpr int kTB = kTok / 32;  // 32-token MFMA blocks per workgroup
+constexpr int kChunkSplit = 1;  // workgroups that share one token block's channel chunks
 constexpr int kOut = 128;  // output channels per chunk
 constexpr int kMaxK = 512; // padded patch length the LDS tile holds
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
+// KSC: the number of 16-wide k-steps (Kp/16) when it is at most 8, so the W
+// operands of a chunk sit in registers and the next chunk's can be
+// prefetched; 0 selects a generic path that loads W step by step.
+template <int KSC>
 __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ w,
                                                             const uint16_t *__restrict__ bias,
                                                             uint16_t *__restrict__ tok, PatchGeom g, int K,
                                                             int Kp)
 {
-    // A tile: [kTok][Kp + 8] bf16 (the 16-byte pad staggers rows over banks).
-    __shared__ __attribute__((aligned(16))) unsigned char a_lds[kTok * (kMaxK + 8) * 2];
-    // Output chunk: [kTok][kOut + 8] bf16.
-    __shared__ __attribute__((aligned(16))) unsigned char o_lds[kTok * (kOut + 8) * 2];
-    lds_u8 *al = (lds_u8 *)a_lds;
-    lds_u8 *ol = (lds_u8 *)o_lds;
+    // Dynamic LDS, sized to the patch length: the output chunk
+    // [kTok][kOut + 8] bf16, then the A tile [kTok][Kp + 8] bf16 (the 16-byte
+    // pads stagger rows over banks).
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     const int arow = (Kp + 8) * 2;     // bytes per A row
     const int orow = (kOut + 8) * 2;   // bytes per output-chunk row
+    lds_u8 *ol = (lds_u8 *)dyn_lds;
+    lds_u8 *al = ol + kTok * orow;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -52,50 +59,107 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     const int64_t M = (int64_t)g.B * N;
     const int64_t m0 = (int64_t)blockIdx.x * kTok;
 
-    // Gather the patch matrix (zero past K and past the last token).
-    for (int idx = tid; idx < kTok * Kp; idx += 256) {
-        const int r = idx / Kp, kk = idx % Kp;
+    // Gather the patch matrix (zero past K and past the last token). Each
+    // thread owns one token and a run of KR = Kp / (256 / kTok) consecutive
+    // patch indices: the token's (b, t, h, w) is decomposed once and the
+    // patch index (c, i, j, kw) advances by carries, so the index math is a
+    // few adds per element.
+    {
+        constexpr int TPT = 256 / kTok;  // threads per token
+        const int r = tid / TPT;
+        const int KR = Kp / TPT;
+        const int kk0 = (tid % TPT) * KR;
         const int64_t m = m0 + r;
-        uint16_t val = 0;
-        if (m < M && kk < K) {
-            const int kw = kk % g.pw, j = (kk / g.pw) % g.ph, i = (kk / (g.pw * g.ph)) % g.pt;
-            const int c = kk / (g.pw * g.ph * g.pt);
+        lds_u8 *arow_p = al + r * arow;
+        if (m < M) {
             const int64_t b = m / N, n = m % N;
-            const int64_t t = n / ((int64_t)g.Hp * g.Wp);
-            const int64_t hh = (n / g.Wp) % g.Hp, ww = n % g.Wp;
-            val = x[(((b * g.C + c) * g.Tl + t * g.pt + i) * g.Hl + hh * g.ph + j) * g.Wl + ww * g.pw + kw];
+            const int t = (int)(n / ((int64_t)g.Hp * g.Wp));
+            const int hh = (int)((n / g.Wp) % g.Hp), ww = (int)(n % g.Wp);
+            const uint16_t *xb = x + (((b * g.C) * g.Tl + (int64_t)t * g.pt) * g.Hl + (int64_t)hh * g.ph) * g.Wl +
+                                 (int64_t)ww * g.pw;
+            int kw = kk0 % g.pw, j = (kk0 / g.pw) % g.ph, i = (kk0 / (g.pw * g.ph)) % g.pt;
+            int c = kk0 / (g.pw * g.ph * g.pt);
+            for (int e = 0; e < KR; ++e) {
+                const int kk = kk0 + e;
+                uint16_t val = 0;
+                if (kk < K) val = xb[(((int64_t)c * g.Tl + i) * g.Hl + j) * g.Wl + kw];
+                *(__attribute__((address_space(3))) uint16_t *)(arow_p + kk * 2) = val;
+                if (++kw == g.pw) {
+                    kw = 0;
+                    if (++j == g.ph) {
+                        j = 0;
+                        if (++i == g.pt) {
+                            i = 0;
+                            ++c;
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int e = 0; e < KR; ++e) *(__attribute__((address_space(3))) uint16_t *)(arow_p + (kk0 + e) * 2) = 0;
         }
-        *(__attribute__((address_space(3))) uint16_t *)(al + r * arow + kk * 2) = val;
     }
     __syncthreads();
 
     const bool kvec = (K % 8) == 0;  // W rows can be read as 16-byte vectors
-    for (int oc = 0; oc < g.Dout; oc += kOut) {
-        f32x16 acc[2] = {(f32x16){}, (f32x16){}};
-        const int orow_w = oc + wave * 32 + col;  // W row this lane feeds
-        for (int s = 0; s < Kp / 16; ++s) {
-            const int k0 = 16 * s + 8 * half;
-            bf16x8 wa = (bf16x8){};
-            if (orow_w < g.Dout) {
-                if (kvec) {
-                    if (k0 < K) wa = *(const bf16x8 *)(w + (int64_t)orow_w * K + k0);
-                } else {
-                    uint16_t e8[8];
+    // This workgroup's channel chunks: kOut-wide chunks c0, c0 + 1, ..., c1 - 1.
+    const int nchunks = (g.Dout + kOut - 1) / kOut;
+    const int per = (nchunks + gridDim.y - 1) / gridDim.y;
+    const int c0 = blockIdx.y * per, c1 = min(nchunks, c0 + per);
+    // W operands (A of C^T = W A^T) of chunk oc, step s2: lane row
+    // oc + wave*32 + col, features 16*s2 + 8*half .. +8.
+    auto w_op = [&](int oc, int s2) {
+        const int orow_w = oc + wave * 32 + col;
+        const int k0 = 16 * s2 + 8 * half;
+        bf16x8 v8 = (bf16x8){};
+        if (orow_w < g.Dout) {
+            if (kvec) {
+                if (k0 < K) v8 = *(const bf16x8 *)(w + (int64_t)orow_w * K + k0);
+            } else {
+                uint16_t e8[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) e8[e] = (k0 + e < K) ? w[(int64_t)orow_w * K + k0 + e] : 0;
-                    wa = __builtin_bit_cast(bf16x8, e8);
-                }
+                for (int e = 0; e < 8; ++e) e8[e] = (k0 + e < K) ? w[(int64_t)orow_w * K + k0 + e] : 0;
+                v8 = __builtin_bit_cast(bf16x8, e8);
             }
+        }
+        return v8;
+    };
+    constexpr int NS = KSC > 0 ? KSC : 1;
+    bf16x8 wcur[NS], wnext[NS];
+    if constexpr (KSC > 0) {
+        if (c0 < c1)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
+            for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = w_op(c0 * kOut, s2);
+    }
+    for (int ci = c0; ci < c1; ++ci) {
+        const int oc = ci * kOut;
+        f32x16 acc[kTB];
+#pragma unroll
+        for (int tb = 0; tb < kTB; ++tb) acc[tb] = (f32x16){};
+        auto step = [&](int s2, const bf16x8 &wa) {
+            const int k0 = 16 * s2 + 8 * half;
+#pragma unroll
+            for (int tb = 0; tb < kTB; ++tb) {
                 const bf16x8 bt = *(const __attribute__((address_space(3))) bf16x8 *)(
                     al + (tb * 32 + col) * arow + k0 * 2);
                 acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc[tb], 0, 0, 0);
             }
+        };
+        if constexpr (KSC > 0) {
+            // The next chunk's W loads are in flight during this chunk.
+            if (ci + 1 < c1)
+#pragma unroll
+                for (int s2 = 0; s2 < KSC; ++s2) wnext[s2] = w_op(oc + kOut, s2);
+#pragma unroll
+            for (int s2 = 0; s2 < KSC; ++s2) step(s2, wcur[s2]);
+#pragma unroll
+            for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = wnext[s2];
+        } else {
+            for (int s2 = 0; s2 < Kp / 16; ++s2) step(s2, w_op(oc, s2));
         }
         // acc[tb]: lane holds token tb*32+col, channels wave*32 + 8*(r/4) + 4*half + r%4.
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < kTB; ++tb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int oo = wave * 32 + 8 * r4 + 4 * half;  // channel within the chunk
@@ -120,7 +184,7 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
                 *(u32x4 *)(tok + m * g.Dout + o0) = *(const __attribute__((address_space(3))) u32x4 *)(
                     ol + r * orow + ch * 16);
         }
-        __syncthreads();
+        __syncthreads();  // the output chunk is reused by the next chunk
     }
 }
 
@@ -157,10 +221,29 @@ hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, 
     const int Kp = (K + 15) / 16 * 16;
     if (Kp > kMaxK || g.Dout % 8) return hipErrorInvalidValue;
     const int64_t M = (int64_t)g.B * g.T * g.Hp * g.Wp;
-    const uint32_t grid = (uint32_t)((M + kTok - 1) / kTok);
-    hipLaunchKernelGGL(patchify_bf16_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)w, (const uint16_t *)bias, (uint16_t *)tok, g, K, Kp);
-    return hipGetLastError();
+    const dim3 grid((uint32_t)((M + kTok - 1) / kTok), kChunkSplit);
+    const size_t lds = (size_t)kTok * ((kOut + 8) + (Kp + 8)) * 2;
+    auto go = [&](auto kernel) {
+        if (lds > 65536) {  // above the default dynamic-LDS limit (up to 50 KB at Kp = 512)
+            const hipError_t e =
+                hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(kernel, grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)w,
+                           (const uint16_t *)bias, (uint16_t *)tok, g, K, Kp);
+        return hipGetLastError();
+    };
+    switch (Kp / 16) {
+        case 1: return go(patchify_bf16_kernel<1>);
+        case 2: return go(patchify_bf16_kernel<2>);
+        case 3: return go(patchify_bf16_kernel<3>);
+        case 4: return go(patchify_bf16_kernel<4>);
+        case 5: return go(patchify_bf16_kernel<5>);
+        case 6: return go(patchify_bf16_kernel<6>);
+        case 7: return go(patchify_bf16_kernel<7>);
+        case 8: return go(patchify_bf16_kernel<8>);
+        default: return go(patchify_bf16_kernel<0>);
+    }
 }
 
 hipError_t launch_patchify_f32(const float *x, const float *w, const float *bias, float *tok, const PatchGeom &g,
