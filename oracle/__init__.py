@@ -72,6 +72,10 @@ def _load():
                                                                             ctypes.POINTER(ctypes.c_int64),
                                                                             ctypes.c_int64]
         lib.oracle_cross_attention.restype = i
+        lib.oracle_window_attention.argtypes = [dp, dp, dp, dp] + [i] * 9 + [ctypes.c_double,
+                                                                             ctypes.POINTER(ctypes.c_int64),
+                                                                             ctypes.c_int64]
+        lib.oracle_window_attention.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -174,6 +178,26 @@ def cross_attention(q, k, v, scale: float = 0.0, rows: Optional[np.ndarray] = No
     out = np.empty((B, nrows, heads, D), dtype=np.float64)
     _check(_load().oracle_cross_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, Nq, Nk, heads, D,
                                           float(scale), rp, nrows))
+    return out
+
+
+def window_attention(q, k, v, grid: Tuple[int, int, int], window: Tuple[int, int, int],
+                     scale: float = 0.0, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Attention within non-overlapping (wt, wh, ww) spacetime windows."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, heads, D = q.shape
+    T, Hp, Wp = grid
+    if N != T * Hp * Wp or k.shape != q.shape or v.shape != q.shape:
+        raise OracleError("q/k/v shapes do not match the grid")
+    if rows is None:
+        rp, nrows = None, N
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        rp, nrows = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), int(rows.size)
+    out = np.empty((B, nrows, heads, D), dtype=np.float64)
+    wt, wh, ww = window
+    _check(_load().oracle_window_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, T, Hp, Wp, heads, D,
+                                           int(wt), int(wh), int(ww), float(scale), rp, nrows))
     return out
 
 

@@ -308,6 +308,94 @@ int oracle_cross_attention(const double *q, const double *k, const double *v, do
     return failed ? ORACLE_E_NOMEM : ORACLE_OK;
 }
 
+/* ------------------------------------------------------------------------
+ * Windowed spacetime attention: the (T, Hp, Wp) token grid is cut into
+ * non-overlapping windows of wt x wh x ww tokens (the last window along an
+ * axis is cut short by the grid), and each token attends to the tokens of its
+ * own window. This restricts attention to local spacetime windows, the lever
+ * "Video Diffusion Models, in depth" ("Inference: where the time goes")
+ * names against the quadratic term. Windows (1, Hp, Wp) give the spatial
+ * pass, (T, 1, 1) the temporal pass and (T, Hp, Wp) full attention.
+ *   key set of (t, h, w) = {(t', h', w') : t'/wt = t/wt, h'/wh = h/wh, w'/ww = w/ww}
+ * q/k/v/o and rows as in oracle_attention.
+ * ------------------------------------------------------------------------ */
+int oracle_window_attention(const double *q, const double *k, const double *v, double *o,
+                            int B, int T, int Hp, int Wp, int heads, int D, int wt, int wh, int ww,
+                            double scale, const int64_t *rows, int64_t nrows)
+{
+    if (!q || !k || !v || !o || B <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || heads <= 0 || D <= 0 ||
+        wt <= 0 || wh <= 0 || ww <= 0)
+        return ORACLE_E_ARG;
+    const int64_t HW = (int64_t)Hp * Wp;
+    const int64_t N = (int64_t)T * HW;
+    if (rows == NULL && nrows != N)
+        return ORACLE_E_ARG;
+    if (nrows <= 0)
+        return ORACLE_E_ARG;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return ORACLE_E_ARG;
+    if (scale <= 0.0)
+        scale = 1.0 / sqrt((double)D);
+    int failed = 0;
+
+    #pragma omp parallel
+    {
+        double *logit = (double *)malloc(sizeof(double) * (size_t)N);
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!logit || !key || !acc) {
+            #pragma omp atomic write
+            failed = 1;
+        }
+        #pragma omp for schedule(dynamic, 4) collapse(3)
+        for (int b = 0; b < B; ++b)
+            for (int hd = 0; hd < heads; ++hd)
+                for (int64_t r = 0; r < nrows; ++r) {
+                    if (!logit || !key || !acc)
+                        continue;
+                    const int64_t n = rows ? rows[r] : r;
+                    const int t = (int)(n / HW), h = (int)((n / Wp) % Hp), w = (int)(n % Wp);
+                    /* The key set: every token whose window indices match. */
+                    int64_t nk = 0;
+                    for (int64_t m = 0; m < N; ++m) {
+                        const int tm = (int)(m / HW), hm = (int)((m / Wp) % Hp), wm = (int)(m % Wp);
+                        if (tm / wt == t / wt && hm / wh == h / wh && wm / ww == w / ww)
+                            key[nk++] = m;
+                    }
+                    const double *qn = q + (((int64_t)b * N + n) * heads + hd) * D;
+                    double M = -INFINITY;
+                    for (int64_t i = 0; i < nk; ++i) {
+                        const double *km = k + (((int64_t)b * N + key[i]) * heads + hd) * D;
+                        double dot = 0.0;
+                        for (int d = 0; d < D; ++d)
+                            dot += qn[d] * km[d];
+                        logit[i] = scale * dot;
+                        if (logit[i] > M)
+                            M = logit[i];
+                    }
+                    double sum = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        acc[d] = 0.0;
+                    for (int64_t i = 0; i < nk; ++i) {
+                        const double wgt = exp(logit[i] - M);
+                        const double *vm = v + (((int64_t)b * N + key[i]) * heads + hd) * D;
+                        sum += wgt;
+                        for (int d = 0; d < D; ++d)
+                            acc[d] += wgt * vm[d];
+                    }
+                    double *on = o + (((int64_t)b * nrows + r) * heads + hd) * D;
+                    for (int d = 0; d < D; ++d)
+                        on[d] = acc[d] / sum;
+                }
+        free(logit);
+        free(key);
+        free(acc);
+    }
+    return failed ? ORACLE_E_NOMEM : ORACLE_OK;
+}
+
 /* Number of threads OpenMP will use for the routines above. */
 int oracle_num_threads(void)
 {

@@ -359,3 +359,38 @@ def test_cross_closed_forms():
                                rtol=1e-13, atol=1e-14)
     rows = np.array([0, 5, 8], dtype=np.int64)
     np.testing.assert_array_equal(oracle.cross_attention(q, k, v, rows=rows), oracle.cross_attention(q, k, v)[:, rows])
+
+
+# ----------------------------------------------------------------------------
+# Windowed spacetime attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("grid,window", [((4, 6, 7), (2, 3, 3)), ((5, 4, 9), (3, 4, 2)), ((3, 5, 5), (1, 2, 5)),
+                                         ((2, 3, 4), (5, 5, 5))])
+def test_window_matches_masked_sdpa(grid, window):
+    T, Hp, Wp = grid
+    wt, wh, ww = window
+    N = T * Hp * Wp
+    t, h, w = _grid_coords(T, Hp, Wp)
+    same = ((t[:, None] // wt == t[None, :] // wt) & (h[:, None] // wh == h[None, :] // wh)
+            & (w[:, None] // ww == w[None, :] // ww))
+    q, k, v = _qkv(2, N, 2, 32)
+    np.testing.assert_allclose(oracle.window_attention(q, k, v, grid, window), _sdpa(q, k, v, same),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_window_special_cases():
+    grid = (3, 4, 5)
+    T, Hp, Wp = grid
+    q, k, v = _qkv(1, 60, 2, 32)
+    np.testing.assert_allclose(oracle.window_attention(q, k, v, grid, (1, Hp, Wp)),
+                               oracle.attention(q, k, v, grid, "spatial"), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.window_attention(q, k, v, grid, (T, 1, 1)),
+                               oracle.attention(q, k, v, grid, "temporal"), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.window_attention(q, k, v, grid, (T, Hp, Wp)),
+                               oracle.attention(q, k, v, grid, "full"), rtol=1e-13, atol=1e-15)
+    # 1x1x1 windows: each token attends to itself only.
+    np.testing.assert_array_equal(oracle.window_attention(q, k, v, grid, (1, 1, 1)), v)
+    rows = np.array([0, 17, 59], dtype=np.int64)
+    np.testing.assert_array_equal(oracle.window_attention(q, k, v, grid, (2, 3, 2), rows=rows),
+                                  oracle.window_attention(q, k, v, grid, (2, 3, 2))[:, rows])
