@@ -213,7 +213,7 @@ def main():
         "cpu_baseline": None,
     }
 
-    result["next_rows"] = {"cross": bench_cross(vd, torch)}
+    result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
     print(json.dumps(result), flush=True)
@@ -239,6 +239,39 @@ def bench_cross(vd, torch, iters: int = 20):
     ms = a.elapsed_time(b) / iters
     flop = 4.0 * w.B * w.heads * w.Nq * w.Nk * w.head_dim
     return {"workload": f"q [{w.B},{w.Nq},{w.heads},{w.head_dim}] x k/v [{w.B},{w.Nk},{w.heads},{w.head_dim}]",
+            "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+
+def window_flop(w, window) -> float:
+    """4*|window|^2*head_dim FLOP per window and head, over the clipped windows."""
+    total = 0
+    for ext, win in zip((w.T, w.Hp, w.Wp), window):
+        sizes = [min(win, ext - s) for s in range(0, ext, win)]
+        total = sizes if total == 0 else [a * b for a in total for b in sizes]
+    return 4.0 * w.B * w.heads * w.head_dim * float(sum(n * n for n in total))
+
+
+def bench_window(vd, torch, iters: int = 20):
+    """Windowed attention, timed on its own after the step: the 480p grid cut
+    into 3 x 15 x 26 windows (28 windows of 1,170 tokens), 12 heads x 128."""
+    from synthetic_inputs import WORKLOADS
+    w = WORKLOADS["480p_window"]
+    grid = (w.T, w.Hp, w.Wp)
+    d = w.draw_qkv()
+    q, k, v = (_dev(d[n]) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    for _ in range(3):
+        vd.attn_window(q, k, v, grid, w.window, out=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        vd.attn_window(q, k, v, grid, w.window, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    flop = window_flop(w, w.window)
+    return {"workload": f"[{w.B},{w.N},{w.heads},{w.head_dim}] grid {grid} windows {w.window}",
             "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 

@@ -13,7 +13,9 @@
  *   vdit_attn_temporal  the same, with keys limited to the query's own patch
  *                       position across frames;
  *   vdit_attn_cross     attention from the video tokens to another token set
- *                       (the text prompt).
+ *                       (the text prompt);
+ *   vdit_attn_window    the same, with keys limited to the query's own
+ *                       non-overlapping wt x wh x ww spacetime window.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -192,6 +194,29 @@ vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, vo
 vdit_status_t vdit_attn_cross(const void *q, const void *k, const void *v, void *o,
                               int B, int heads, int Nq, int Nk, int head_dim,
                               float scale, vdit_dtype_t dtype, void *stream);
+
+/*
+ * vdit_attn_window — attention within local spacetime windows.
+ *
+ * "Video Diffusion Models, in depth", "Inference: where the time goes":
+ * limiting attention to local windows of space and time is the direct
+ * attack on the quadratic term. Reading taken here: the grid is cut into
+ * non-overlapping windows of wt x wh x ww tokens, the last window along an
+ * axis cut short by the grid, and the keys of query (t, h, w) are the tokens
+ * (t', h', w') with t'/wt = t/wt, h'/wh = h/wh and w'/ww = w/ww (integer
+ * division):
+ *   o[b][n][h] = sum_{m in window(n)} softmax_m(scale * <q_n, k_m>) v_m.
+ * Window (1, Hp, Wp) is the spatial pass, (T, 1, 1) the temporal pass and
+ * (T, Hp, Wp) full attention. 4*|window|^2*head_dim FLOP per window and head.
+ *
+ * wt, wh, ww : window extents in tokens, >= 1 (else VDIT_E_SHAPE); extents
+ *              larger than the grid are clipped to it.
+ * Other arguments, layouts, limits and errors as vdit_attn_full.
+ */
+vdit_status_t vdit_attn_window(const void *q, const void *k, const void *v, void *o,
+                               int B, int heads, int T, int Hp, int Wp, int head_dim,
+                               int wt, int wh, int ww, float scale, vdit_dtype_t dtype,
+                               void *stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ BF16, F32 = 0, 1
 STATUS = ["VDIT_OK", "VDIT_E_NULL", "VDIT_E_SHAPE", "VDIT_E_HEAD_DIM", "VDIT_E_ROPE_SPLIT",
           "VDIT_E_ALIGN", "VDIT_E_ALIAS", "VDIT_E_DTYPE", "VDIT_E_LAUNCH"]
 EXPORTS = ("vdit_status_str", "vdit_patchify", "vdit_rope3d", "vdit_attn_full",
-           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross")
+           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross", "vdit_attn_window")
 
 
 class VditError(RuntimeError):
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = i
     lib.vdit_attn_cross.argtypes = [vp, vp, vp, vp] + [i] * 5 + [f, i, vp]
     lib.vdit_attn_cross.restype = i
+    lib.vdit_attn_window.argtypes = [vp, vp, vp, vp] + [i] * 9 + [f, i, vp]
+    lib.vdit_attn_window.restype = i
     _lib = lib
     return lib
 
@@ -195,6 +197,27 @@ def attn_cross(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float =
     dt = q.dtype
     _check(lib.vdit_attn_cross(_dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
                                B, heads, Nq, Nk, D, float(scale), _dtype_code(q), _stream(q)))
+    return out
+
+
+def attn_window(q, k, v, grid, window, scale: float = 0.0, out=None) -> torch.Tensor:
+    """Attention within non-overlapping ``window = (wt, wh, ww)`` spacetime
+    windows of the token grid (edge windows clipped by the grid)."""
+    B, N, heads, D = q.shape
+    T, Hp, Wp = grid
+    if N != T * Hp * Wp:
+        raise ValueError("token count does not match the grid")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out has the wrong shape")
+    wt, wh, ww = (int(x) for x in window)
+    lib = load_library()
+    dt = q.dtype
+    _check(lib.vdit_attn_window(_dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
+                                B, heads, T, Hp, Wp, D, wt, wh, ww, float(scale), _dtype_code(q), _stream(q)))
     return out
 
 

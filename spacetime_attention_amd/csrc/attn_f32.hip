@@ -172,6 +172,92 @@ __global__ __launch_bounds__(kQ) void cross_f32_kernel(const float *__restrict__
     }
 }
 
+// Windowed attention in fp32: one thread per (b, window-local query j,
+// head), 64 queries of one window per workgroup; the window's keys are
+// gathered into LDS in tiles. Window-local index j maps to the token
+// (t0 + j/(ch*cw), h0 + (j/cw)%ch, w0 + j%cw) of the window's clipped
+// extents ct x ch x cw.
+template <int D>
+__global__ __launch_bounds__(kQ) void window_f32_kernel(const float *__restrict__ q, const float *__restrict__ k,
+                                                        const float *__restrict__ v, float *__restrict__ o,
+                                                        int heads, WinGeom g, float scale)
+{
+    __shared__ float ks[kTile][D];
+    __shared__ float vs[kTile][D];
+    const int nwin = g.nwt * g.nwh * g.nww;
+    const int qblk = (int)(blockIdx.x % g.nqb);
+    const int hd = (int)((blockIdx.x / g.nqb) % heads);
+    const int seg = (int)(blockIdx.x / ((uint32_t)g.nqb * heads));
+    const int b = seg / nwin, w = seg % nwin;
+    const int iww = w % g.nww, iwh = (w / g.nww) % g.nwh, iwt = w / (g.nww * g.nwh);
+    const int t0 = iwt * g.wt, h0 = iwh * g.wh, w0 = iww * g.ww;
+    const int ct = min(g.wt, g.T - t0), ch = min(g.wh, g.Hp - h0), cw = min(g.ww, g.Wp - w0);
+    const int Lw = ct * ch * cw;
+    if (qblk * kQ >= Lw) return;
+    const int64_t HW = (int64_t)g.Hp * g.Wp;
+    const int64_t org = (int64_t)b * g.T * HW + ((int64_t)t0 * g.Hp + h0) * g.Wp + w0;
+    auto tok = [&](int j) -> int64_t { return org + (j / (ch * cw)) * HW + ((j / cw) % ch) * g.Wp + j % cw; };
+
+    const int j = qblk * kQ + threadIdx.x;
+    const bool valid = j < Lw;
+    float qr[D], acc[D];
+    const float *qp = q + (tok(valid ? j : 0) * heads + hd) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qr[d] = valid ? qp[d] : 0.f;
+        acc[d] = 0.f;
+    }
+    float mx = -INFINITY, l = 0.f;
+    for (int m0 = 0; m0 < Lw; m0 += kTile) {
+        const int nk = (Lw - m0) < kTile ? (Lw - m0) : kTile;
+        for (int i = threadIdx.x; i < nk * D; i += kQ) {
+            const int r = i / D, d = i % D;
+            const int64_t key = tok(m0 + r);
+            ks[r][d] = k[(key * heads + hd) * D + d];
+            vs[r][d] = v[(key * heads + hd) * D + d];
+        }
+        __syncthreads();
+        if (valid)
+            for (int r = 0; r < nk; ++r) {
+                float sc = 0.f;
+#pragma unroll
+                for (int d = 0; d < D; ++d) sc = fmaf(qr[d], ks[r][d], sc);
+                sc *= scale;
+                if (sc > mx) {
+                    const float corr = expf(mx - sc);
+                    l *= corr;
+#pragma unroll
+                    for (int d = 0; d < D; ++d) acc[d] *= corr;
+                    mx = sc;
+                }
+                const float p = expf(sc - mx);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vs[r][d], acc[d]);
+            }
+        __syncthreads();
+    }
+    if (valid) {
+        float *op = o + (tok(j) * heads + hd) * D;
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+    }
+}
+
+template <int D>
+hipError_t launch_window(const float *q, const float *k, const float *v, float *o, int B, int heads,
+                         WinGeom g, float scale, hipStream_t s) {
+    g.nwt = (g.T + g.wt - 1) / g.wt;
+    g.nwh = (g.Hp + g.wh - 1) / g.wh;
+    g.nww = (g.Wp + g.ww - 1) / g.ww;
+    g.nqb = (g.wt * g.wh * g.ww + kQ - 1) / kQ;
+    const uint64_t grid = (uint64_t)B * g.nwt * g.nwh * g.nww * heads * g.nqb;
+    if (grid == 0 || grid > UINT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(window_f32_kernel<D>, dim3((uint32_t)grid), dim3(kQ), 0, s, q, k, v, o, heads, g, scale);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_cross(const float *q, const float *k, const float *v, float *o, int B, int heads, int Nq,
                         int Nk, float scale, hipStream_t s) {
@@ -193,6 +279,16 @@ hipError_t launch(const float *q, const float *k, const float *v, float *o, int 
 }
 
 }  // namespace
+
+hipError_t launch_window_f32(const float *q, const float *k, const float *v, float *o, int B, int heads, int D,
+                             const WinGeom &g, float scale, hipStream_t s) {
+    switch (D) {
+        case 32: return launch_window<32>(q, k, v, o, B, heads, g, scale, s);
+        case 64: return launch_window<64>(q, k, v, o, B, heads, g, scale, s);
+        case 128: return launch_window<128>(q, k, v, o, B, heads, g, scale, s);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_cross_f32(const float *q, const float *k, const float *v, float *o, int B, int heads, int Nq,
                             int Nk, int D, float scale, hipStream_t s) {

@@ -8,6 +8,12 @@
 // clip for full 3D attention, one latent frame (Hp*Wp tokens) for the
 // spatial pass (Lk = L for both), and the whole text prompt for
 // cross-attention ("How AI Generates Video ...", section 5, attn2).
+// Windowed attention ("Video Diffusion Models, in depth", "Inference: where
+// the time goes": attention restricted to local spacetime windows) runs the
+// same tile loop over one wt x wh x ww box of the token grid: its queries and
+// keys are gathered by window-local index j, whose token is found by a
+// mixed-radix decomposition of j over the box's clipped extents, and key
+// rows are advanced by that radix from one 64-key tile to the next.
 //
 // Layout of the work (one workgroup = 4 wavefronts = BM query tokens):
 //  * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
@@ -106,22 +112,25 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// PASS (0 full, 1 spatial, 2 cross) only names the instantiation, so that
-// profiles attribute the passes separately; the code is the same. L is the
-// number of queries and Lk the number of keys per segment (equal for self-
-// attention; the text length for cross-attention).
+// PASS (0 full, 1 spatial, 2 cross, 3 window) names the instantiation, so
+// that profiles attribute the passes separately; the first three run the
+// same code. L is the number of queries and Lk the number of keys per
+// segment (equal for self-attention; the text length for cross-attention);
+// the window pass takes both from the window it works on and nseg = B times
+// the number of windows.
 template <int D, int QB, int NW, int PASS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    uint16_t *__restrict__ o, int nseg, int L, int Lk, int heads, float c)
+    uint16_t *__restrict__ o, int nseg, int L, int Lk, int heads, float c, WinGeom wg)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using S = FlashShape<D, QB, NW>;
+    constexpr bool WIN = PASS == 3;
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * S::TILE];
     lds_u8 *lds = (lds_u8 *)smem;
 
-    const int nqb = (L + S::BM - 1) / S::BM;
-    const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)(nseg * heads * nqb));
+    const int nqb = WIN ? wg.nqb : (L + S::BM - 1) / S::BM;
+    const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)nseg * (uint32_t)heads * (uint32_t)nqb);
     const int qblk = (int)(id % nqb);
     const int hd = (int)((id / nqb) % heads);
     const int seg = (int)(id / ((uint32_t)nqb * heads));
@@ -131,8 +140,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform across the wave
     const int half = lane >> 5, col = lane & 31;
     const int64_t rs = (int64_t)heads * D;  // elements between consecutive tokens
-    const int64_t base = ((int64_t)seg * L * heads + hd) * D;     // query / output rows
-    const int64_t kvbase = ((int64_t)seg * Lk * heads + hd) * D;  // key / value rows
+
+    // Token rows of the queries (qorg) and keys (korg) of this workgroup,
+    // and, for a window, its clipped extents ct x chh x cww and the token
+    // strides of its frame and row.
+    int64_t qorg, korg;
+    int ct = 0, chh = 1, cww = 1, HWt = 0, Wpt = 0;
+    if constexpr (WIN) {
+        const int nwin = wg.nwt * wg.nwh * wg.nww;
+        const int b = seg / nwin, w = seg % nwin;
+        const int iww = w % wg.nww, iwh = (w / wg.nww) % wg.nwh, iwt = w / (wg.nww * wg.nwh);
+        const int t0 = iwt * wg.wt, h0 = iwh * wg.wh, w0 = iww * wg.ww;
+        ct = min(wg.wt, wg.T - t0);
+        chh = min(wg.wh, wg.Hp - h0);
+        cww = min(wg.ww, wg.Wp - w0);
+        HWt = wg.Hp * wg.Wp;
+        Wpt = wg.Wp;
+        L = Lk = ct * chh * cww;
+        if (qblk * S::BM >= L) return;  // a block past the end of a clipped window
+        qorg = korg = (int64_t)b * wg.T * HWt + ((int64_t)t0 * wg.Hp + h0) * wg.Wp + w0;
+    } else {
+        qorg = (int64_t)seg * L;
+        korg = (int64_t)seg * Lk;
+    }
+    // Token (relative to the origin) of window-local index j.
+    auto tok = [&](int j) -> int {
+        if constexpr (WIN)
+            return (j / (chh * cww)) * HWt + ((j / cww) % chh) * Wpt + j % cww;
+        else
+            return j;
+    };
+    const int64_t base = (qorg * heads + hd) * D;    // query / output rows
+    const int64_t kvbase = (korg * heads + hd) * D;  // key / value rows
     const uint16_t *qp = q + base, *kp = k + kvbase, *vp = v + kvbase;
     uint16_t *op = o + base;
 
@@ -142,10 +181,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qi = q0 + qb * 32 + col;
+        const int64_t qrow = (int64_t)tok(qi < L ? qi : 0) * rs;
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks) {
             if (qi < L)
-                qop[qb][ks] = *(const bf16x8 *)(qp + qi * rs + 16 * ks + 8 * half);
+                qop[qb][ks] = *(const bf16x8 *)(qp + qrow + 16 * ks + 8 * half);
             else
                 qop[qb][ks] = (bf16x8){};
         }
@@ -153,7 +193,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
     // Buffer descriptors over this (segment, head)'s keys and values: the
     // size stops at the end of key Lk-1's row, so any row >= Lk reads as zero.
-    const int nrec = (int)(((int64_t)(Lk - 1) * rs + D) * 2);
+    const int nrec = (int)(((int64_t)tok(Lk - 1) * rs + D) * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kp, 0, nrec, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vp, 0, nrec, kBufferFlags);
     // Per-lane byte offsets (within a tile) of the chunks this lane fetches:
@@ -168,16 +208,59 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         koff[i] = (uint32_t)(r * rs * 2 + (pc ^ (swz_k<D>(r, 0))) * 16);
         voff[i] = (uint32_t)(r * rs * 2 + (pc ^ (swz_v<D>(r, 0))) * 16);
     }
+    // Window pass: the key index j of each load's row is carried as mixed-
+    // radix digits (jt, jh, jw) over the extents (ct, chh, cww); koff/voff
+    // then hold only the chunk parts, and one tile step adds 64 = dt*chh*cww
+    // + dh*cww + dw with single carries (every digit sum stays below twice
+    // its radix). Rows with jt >= ct (j >= Lk) get an offset past the
+    // descriptor's size and read as zeros.
+    int jt[S::LOADS], jh[S::LOADS], jw[S::LOADS];
+    int dt = 0, dh = 0, dw = 0;
+    if constexpr (WIN) {
+        const int plane = chh * cww;
+        dt = kBN / plane;
+        dh = (kBN % plane) / cww;
+        dw = (kBN % plane) % cww;
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int r = RPL * (wave * S::LOADS + i) + lane / S::CH;
+            koff[i] -= (uint32_t)(r * rs * 2);
+            voff[i] -= (uint32_t)(r * rs * 2);
+            jt[i] = r / plane;
+            jh[i] = (r / cww) % chh;
+            jw[i] = r % cww;
+        }
+    }
+    const uint32_t rsb = (uint32_t)(rs * 2), HWb = (uint32_t)HWt * rsb, Wpb = (uint32_t)Wpt * rsb;
     auto load_tile = [&](int t0, int buf) {
         lds_u8 *kb = lds + buf * 2 * S::TILE;
         lds_u8 *vb = kb + S::TILE;
-        const uint32_t so = (uint32_t)((int64_t)t0 * rs * 2);
+        if constexpr (WIN) {
 #pragma unroll
-        for (int i = 0; i < S::LOADS; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(kb + (wave * S::LOADS + i) * 1024), 16,
-                                                     koff[i], so, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(vb + (wave * S::LOADS + i) * 1024), 16,
-                                                     voff[i], so, 0, 0);
+            for (int i = 0; i < S::LOADS; ++i) {
+                const uint32_t row =
+                    jt[i] < ct ? (uint32_t)jt[i] * HWb + (uint32_t)jh[i] * Wpb + (uint32_t)jw[i] * rsb : 0x80000000u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(kb + (wave * S::LOADS + i) * 1024), 16,
+                                                         row + koff[i], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(vb + (wave * S::LOADS + i) * 1024), 16,
+                                                         row + voff[i], 0, 0, 0);
+                jw[i] += dw;
+                const int cw1 = jw[i] >= cww;
+                jw[i] -= cw1 ? cww : 0;
+                jh[i] += dh + cw1;
+                const int ch1 = jh[i] >= chh;
+                jh[i] -= ch1 ? chh : 0;
+                jt[i] += dt + ch1;
+            }
+        } else {
+            const uint32_t so = (uint32_t)((int64_t)t0 * rs * 2);
+#pragma unroll
+            for (int i = 0; i < S::LOADS; ++i) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void *)(kb + (wave * S::LOADS + i) * 1024), 16,
+                                                         koff[i], so, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void *)(vb + (wave * S::LOADS + i) * 1024), 16,
+                                                         voff[i], so, 0, 0);
+            }
         }
     };
 
@@ -361,6 +444,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         const float inv = 1.0f / pair_sum(lsum[qb]);
         const int qi = q0 + qb * 32 + col;
         if (qi < L) {
+            const int64_t orow = (int64_t)tok(qi) * rs;
 #pragma unroll
             for (int db = 0; db < S::DB; ++db)
 #pragma unroll
@@ -369,7 +453,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
                     u32x2 w;
                     w[0] = pack_bf16x2(oacc[db][qb][4 * r4 + 0] * inv, oacc[db][qb][4 * r4 + 1] * inv);
                     w[1] = pack_bf16x2(oacc[db][qb][4 * r4 + 2] * inv, oacc[db][qb][4 * r4 + 3] * inv);
-                    *(u32x2 *)(op + qi * rs + d) = w;
+                    *(u32x2 *)(op + orow + d) = w;
                 }
         }
     }
@@ -378,13 +462,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
 template <int D, int QB, int NW, int PASS>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
-                  int heads, float c, hipStream_t s) {
+                  int heads, float c, hipStream_t s, WinGeom wg = WinGeom{}) {
     using S = FlashShape<D, QB, NW>;
+    if (PASS == 3) {
+        // L is the largest window's token count; nseg = B * windows.
+        wg.nqb = (L + S::BM - 1) / S::BM;
+    }
     const int nqb = (L + S::BM - 1) / S::BM;
-    const uint32_t grid = (uint32_t)nseg * heads * nqb;
-    hipLaunchKernelGGL((flash_fwd_bf16<D, QB, NW, PASS>), dim3(grid), dim3(S::THREADS), 0, s,
+    const uint64_t grid = (uint64_t)nseg * heads * nqb;
+    if (grid == 0 || grid > UINT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((flash_fwd_bf16<D, QB, NW, PASS>), dim3((uint32_t)grid), dim3(S::THREADS), 0, s,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
-                       nseg, L, Lk, heads, c);
+                       nseg, L, Lk, heads, c, wg);
     return hipGetLastError();
 }
 
@@ -402,6 +491,19 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
         if (pass == 1) return launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
         return launch<64, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
     }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_window_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int D,
+                              const WinGeom &g, float scale_log2e, hipStream_t s) {
+    WinGeom wg = g;
+    wg.nwt = (g.T + g.wt - 1) / g.wt;
+    wg.nwh = (g.Hp + g.wh - 1) / g.wh;
+    wg.nww = (g.Wp + g.ww - 1) / g.ww;
+    const int nseg = B * wg.nwt * wg.nwh * wg.nww;
+    const int Lmax = g.wt * g.wh * g.ww;  // extents are already clipped to the grid
+    if (D == 128) return launch<128, 1, kSpatialWaves, 3>(q, k, v, o, nseg, Lmax, Lmax, heads, scale_log2e, s, wg);
+    if (D == 64) return launch<64, 1, kSpatialWaves, 3>(q, k, v, o, nseg, Lmax, Lmax, heads, scale_log2e, s, wg);
     return hipErrorInvalidValue;
 }
 

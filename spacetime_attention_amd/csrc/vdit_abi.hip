@@ -132,6 +132,42 @@ vdit_status_t vdit_attn_cross(const void *q, const void *k, const void *v, void 
     return launch_status(launch_flash_bf16(q, k, v, o, B, Nq, Nk, heads, D, (float)((double)s * kLog2e), 2, st));
 }
 
+vdit_status_t vdit_attn_window(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
+                               int Hp, int Wp, int head_dim, int wt, int wh, int ww, float scale, vdit_dtype_t dtype,
+                               void *stream) {
+    if (!q || !k || !v || !o) return VDIT_E_NULL;
+    if (dtype != VDIT_BF16 && dtype != VDIT_F32) return VDIT_E_DTYPE;
+    if (B <= 0 || heads <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || head_dim <= 0 || wt <= 0 || wh <= 0 || ww <= 0)
+        return VDIT_E_SHAPE;
+    const int D = head_dim;
+    if (dtype == VDIT_BF16 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    if (dtype == VDIT_F32 && D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    uint64_t n_tok = 1;
+    if (!mul_ok(n_tok, T) || !mul_ok(n_tok, Hp) || !mul_ok(n_tok, Wp)) return VDIT_E_SHAPE;
+    if (n_tok > (uint64_t)INT32_MAX) return VDIT_E_SHAPE;
+    uint64_t elems = n_tok;
+    if (!mul_ok(elems, B) || !mul_ok(elems, heads) || !mul_ok(elems, D)) return VDIT_E_SHAPE;
+    const uint64_t bytes = elems * (uint64_t)esize(dtype);
+    // Windows larger than the grid are clipped to it.
+    WinGeom g{T, Hp, Wp, wt < T ? wt : T, wh < Hp ? wh : Hp, ww < Wp ? ww : Wp, 0, 0, 0, 0};
+    const uint64_t nwin = (uint64_t)((T + g.wt - 1) / g.wt) * ((Hp + g.wh - 1) / g.wh) * ((Wp + g.ww - 1) / g.ww);
+    const uint64_t lw = (uint64_t)g.wt * g.wh * g.ww;
+    // Workgroups (at most 64 queries of one window and head each) must fit a
+    // 1-D grid; windows per batch times B must fit an int.
+    if ((uint64_t)B * nwin > (uint64_t)INT32_MAX || (uint64_t)B * nwin * heads * ((lw + 63) / 64) > UINT32_MAX)
+        return VDIT_E_SHAPE;
+    if (dtype == VDIT_BF16 && n_tok * (uint64_t)heads * (uint64_t)D * 2u >= (uint64_t(1) << 31)) return VDIT_E_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VDIT_E_ALIGN;
+    if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
+        return VDIT_E_ALIAS;
+    const float s = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == VDIT_F32)
+        return launch_status(
+            launch_window_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, B, heads, D, g, s, st));
+    return launch_status(launch_window_bf16(q, k, v, o, B, heads, D, g, (float)((double)s * kLog2e), st));
+}
+
 vdit_status_t vdit_patchify(const void *latent, const void *weight, const void *bias, void *tokens, int B, int C,
                             int pt, int ph, int pw, int Tl, int Hl, int Wl, int heads, int T, int Hp, int Wp,
                             int head_dim, vdit_dtype_t dtype, void *stream) {

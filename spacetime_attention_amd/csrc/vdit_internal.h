@@ -51,6 +51,19 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
                              int L, int Lk, int heads, int D, float scale_log2e, int pass,
                              hipStream_t s);
 
+// Non-overlapping spacetime windows over a (T, Hp, Wp) token grid: window
+// (iwt, iwh, iww) holds tokens t in [iwt*wt, min((iwt+1)*wt, T)) and likewise
+// for h and w; its queries attend to exactly its tokens. wt/wh/ww are clipped
+// to the grid by the caller; nwt/nwh/nww (windows per axis) and nqb (query
+// blocks per window) are filled in by the launcher.
+struct WinGeom {
+    int T, Hp, Wp, wt, wh, ww, nwt, nwh, nww, nqb;
+};
+hipError_t launch_window_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int D,
+                              const WinGeom &g, float scale_log2e, hipStream_t s);
+hipError_t launch_window_f32(const float *q, const float *k, const float *v, float *o, int B, int heads, int D,
+                             const WinGeom &g, float scale, hipStream_t s);
+
 // fp32 attention with a generic key set: query token n of batch b has keys
 // key(m) = kbase(n) + m*kstride, m < nkeys, where for mode 0 (full)
 // kbase = b*N, kstride = 1, nkeys = N; mode 1 (spatial) kbase = b*N + t*HW,

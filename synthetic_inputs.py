@@ -130,6 +130,7 @@ class Workload:
     latent_std: float = 1.0
     weight_std: float = 0.02
     rope_split: Optional[Tuple[int, int, int]] = None
+    window: Optional[Tuple[int, int, int]] = None
 
     @property
     def N(self) -> int:
@@ -183,6 +184,10 @@ WORKLOADS: Dict[str, Workload] = {
     "block_input": Workload("block_input", B=1, T=21, Hp=30, Wp=52, heads=12, head_dim=128,
                             dtype="bf16", seed=4, C=16, patch=(1, 2, 2),
                             rope_split=(44, 42, 42)),
+    # Windowed attention on the 480p grid: windows of 3 latent frames x half
+    # the frame height x half its width, 3 x 15 x 26 = 1,170 tokens, 28 windows.
+    "480p_window": Workload("480p_window", B=1, T=21, Hp=30, Wp=52, heads=12, head_dim=128,
+                            dtype="bf16", seed=6, window=(3, 15, 26)),
 }
 
 

@@ -113,3 +113,22 @@ def test_cross_argument_errors(lib):
     assert call(v=V + 8) == 5
     assert call(o=K + 16) == 6                    # o overlaps k
     assert call(dt=9) == 7
+
+
+def test_window_argument_errors(lib):
+    f = lib.vdit_attn_window
+
+    def call(q=Q, k=K, v=V, o=O, B=1, heads=2, T=3, Hp=4, Wp=5, D=128, wt=2, wh=2, ww=2, scale=0.0,
+             dt=vd.BF16):
+        return f(q, k, v, o, B, heads, T, Hp, Wp, D, wt, wh, ww, scale, dt, None)
+
+    assert call(o=None) == 1
+    assert call(wt=0) == 2                        # a window extent below 1
+    assert call(ww=-2) == 2
+    assert call(T=0) == 2
+    assert call(T=64, Hp=256, Wp=256, heads=16) == 2  # one batch over 2 GiB in bf16
+    assert call(D=32) == 3
+    assert call(dt=vd.F32, D=80) == 3
+    assert call(k=K + 8) == 5
+    assert call(o=V + 16) == 6
+    assert call(dt=5) == 7

@@ -303,3 +303,84 @@ def test_cross_480p_sampled():
     rows = sample_rows(w.Nq, 127, offset=3)
     ref = oracle.cross_attention(d["q"].f32, d["k"].f32, d["v"].f32, rows=rows)
     assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", "cross_480p")
+
+
+# ----------------------------------------------------------------------------
+# Windowed spacetime attention
+# ----------------------------------------------------------------------------
+
+WINDOW_SMALL = [
+    # (name, B, grid, window, heads, D)
+    ("ragged_edges", 2, (5, 9, 13), (2, 4, 5), 2, 128),
+    ("multi_tile", 1, (4, 12, 20), (3, 7, 9), 2, 128),
+    ("d64", 1, (6, 7, 11), (4, 3, 6), 3, 64),
+    ("frame_window", 1, (3, 9, 15), (1, 9, 15), 2, 128),
+    ("time_column", 1, (9, 3, 4), (9, 1, 1), 2, 128),
+    ("larger_than_grid", 1, (3, 5, 7), (8, 16, 16), 2, 128),
+    ("one_token", 1, (2, 3, 5), (1, 1, 1), 2, 128),
+    ("thin_rows", 1, (2, 20, 70), (1, 1, 67), 2, 64),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_SMALL, ids=[c[0] for c in WINDOW_SMALL])
+def test_window_small_bf16(case):
+    name, B, grid, window, heads, D = case
+    _announce(f"window bf16 {name} B={B} grid={grid} window={window} heads={heads} D={D}")
+    w = small_grid(name, B, *grid, heads, D, "bf16", seed=200 + len(name))
+    d, (q, k, v) = _qkv(w)
+    got = to_host(vd.attn_window(q, k, v, grid, window))
+    ref = oracle.window_attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, window)
+    assert_close(got, ref, "bf16", f"window/{name}")
+
+
+def test_window_peaky_bf16():
+    grid, window = (4, 9, 14), (3, 5, 6)
+    _announce(f"window peaky bf16 grid={grid} window={window}")
+    w = small_grid("wpeaky", 1, *grid, 2, 128, "bf16", seed=8)
+    d, (q, k, v) = _qkv(w, q_scale=4.0)
+    got = to_host(vd.attn_window(q, k, v, grid, window))
+    ref = oracle.window_attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, window)
+    assert_close(got, ref, "bf16", "window/peaky")
+
+
+def test_window_one_token_is_exact_and_in_bounds():
+    # 1x1x1 windows: each output is its own V bit for bit; guard bands around
+    # the output stay untouched.
+    grid = (3, 5, 7)
+    _announce("window 1x1x1 exactness and guard bands")
+    w = small_grid("w111", 2, *grid, 2, 128, "bf16", seed=9)
+    d, (q, k, v) = _qkv(w)
+    n = q.numel()
+    buf = torch.full((n + 2 * 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[4096:4096 + n].view_as(q)
+    vd.attn_window(q, k, v, grid, (1, 1, 1), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, v)
+    assert bool((buf[:4096] == 7.0).all()) and bool((buf[4096 + n:] == 7.0).all())
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_window_f32(D):
+    grid, window = (5, 6, 7), (2, 4, 3)
+    _announce(f"window f32 D={D} grid={grid} window={window}")
+    w = small_grid("wf32", 2, *grid, 2, D, "f32", seed=12)
+    d, (q, k, v) = _qkv(w)
+    got = to_host(vd.attn_window(q, k, v, grid, window))
+    ref = oracle.window_attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, window)
+    assert_close(got, ref, "f32", f"window/f32/D{D}")
+
+
+@pytest.mark.parametrize("window,stride", [(None, 61), ((4, 8, 8), 89)])
+def test_480p_window_sampled(window, stride):
+    # The benchmark's 3 x 15 x 26 windows (which tile the grid exactly), and
+    # 4 x 8 x 8 windows, which leave clipped windows on every edge of it.
+    w = WORKLOADS["480p_window"]
+    grid = (w.T, w.Hp, w.Wp)
+    window = window or w.window
+    _announce(f"480p window {window} full size, rows every {stride}")
+    d, (q, k, v) = _qkv(w)
+    got = vd.attn_window(q, k, v, grid, window)
+    rows = sample_rows(w.N, stride, offset=stride // 3)
+    got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
+    ref = oracle.window_attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, window, rows=rows)
+    assert_close(got_rows, ref, "bf16", f"480p_window/{window}")
