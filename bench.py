@@ -154,6 +154,10 @@ def main():
     def avg_ms(name):
         return float(np.mean([a.elapsed_time(b) for a, b in ev[name]]))
 
+    def spread(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return {"ms_median": float(np.median(xs)), "ms_min": float(np.min(xs))}
+
     f_full = 4.0 * wf.B * H * wf.N * wf.N * D
     f_spatial = 4.0 * wd.B * H * wd.T * HW * HW * D
     f_temporal = 4.0 * wd.B * H * HW * wd.T * wd.T * D
@@ -181,9 +185,11 @@ def main():
                      "frac_hbm_peak": b_patch / t["patchify"] / 1e6 / PEAK_HBM_GBS,
                      "tflops": f_patch / t["patchify"] / 1e9},
     }
+    for p in passes:
+        per_pass[p].update(spread(p))
 
     achieved = f_full / t["full"] / 1e9
-    roofline = {"kernel": "flash_fwd_bf16<128,1,0> (vdit_attn_full, 480p)", "bound": "mfma",
+    roofline = {"kernel": "flash_fwd_bf16<128,1,8,0> (vdit_attn_full, 480p)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS,
                 "traffic": _traffic("attn_flash.hip", "flash_full_480p")}
@@ -216,6 +222,7 @@ def main():
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
+        result["cpu_baseline"]["gpu_over_cpu"] = per_pass["full"]["tflops"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
 
 
@@ -275,6 +282,16 @@ def bench_window(vd, torch, iters: int = 20):
             "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(df, wf):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     full attention at 480p for every 32nd query token (plus the last) of
@@ -290,7 +307,7 @@ def cpu_baseline(df, wf):
     dt = time.perf_counter() - t0
     flop = 4.0 * wf.B * wf.heads * rows.size * wf.N * wf.head_dim
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": dt,
+            "kind": "oracle", "seconds": dt, "cpu_model": _cpu_model(),
             "sample": f"full attention 480p [1,32760,12,128], {rows.size} query rows "
                       f"(every 32nd token) x 12 heads, fp64 C oracle"}
 
