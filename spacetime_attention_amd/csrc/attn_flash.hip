@@ -37,10 +37,14 @@
 //    issued before the current tile's products. Chunk-XOR swizzles keep the
 //    K reads (32 rows, one 16-byte chunk each) and the transposed V reads
 //    (8 rows x 64 bytes) free of bank conflicts.
-//  * The running maximum is raised only when a tile's maximum exceeds it by
-//    more than 2^8 in the exp2 domain, so the O^T rescale is skipped on most
-//    tiles; normalising by the sum taken against the same reference keeps
-//    the result exactly softmax.
+//  * The reference maximum of the online softmax is raised lazily: a tile's
+//    probabilities are formed against the current reference, and only when
+//    a lane's tile sum exceeds 2^32 (or is not finite, as on the first tile)
+//    does the wave take the row maximum, raise the reference, rescale O^T
+//    and form them again. Most tiles skip the row maximum and the rescale;
+//    normalising by the sum taken against the same reference keeps the
+//    result exactly softmax, and the reference, always an actual score,
+//    never exceeds the true maximum.
 //  * Workgroups are numbered so that each XCD gets a contiguous run of
 //    (segment, head, query block) tiles and so shares K/V in its own L2.
 #include "vdit_internal.h"
@@ -58,7 +62,10 @@ constexpr int kBN = 64;                // keys per LDS tile
 // last query block.
 constexpr int kFullWaves = 8;
 constexpr int kSpatialWaves = 4;
-constexpr float kRescaleSlack = 8.0f;  // log2 units the reference max may lag the true max
+// A tile's probabilities against the reference maximum may sum to at most
+// this before the reference is raised: every probability then stays below
+// 2^32, so fp32 sums and accumulators over any key count stay finite.
+constexpr float kTileSumBudget = 4294967296.0f;
 
 template <int D, int QB, int NW>
 struct FlashShape {
@@ -362,43 +369,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         }
 
         // Online softmax in the exp2 domain: x = s * scale * log2(e).
+        // Probabilities are first formed against the current reference
+        // maximum; only if a lane's tile sum leaves the budget (or is not
+        // finite, as on the first tile) does the wave take the row maximum,
+        // raise the reference, rescale and form them again.
         bf16x8 pop[QB][2][2];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float mx = sacc[0][qb][0];
+            float ls = 0.f;
+            auto probs = [&]() {
+                const float nm = -mref[qb];
+                ls = 0.f;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+                for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
-            mx = pair_max(mx) * c;
-            const bool raise = mx > mref[qb] + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(raise)) {
-                const float mnew = raise ? mx : mref[qb];
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        float p[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
+                            ls += p[e];
+                        }
+                        u32x4 pk;
+                        pk[0] = pack_bf16x2(p[0], p[1]);
+                        pk[1] = pack_bf16x2(p[2], p[3]);
+                        pk[2] = pack_bf16x2(p[4], p[5]);
+                        pk[3] = pack_bf16x2(p[6], p[7]);
+                        pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
+                    }
+            };
+            probs();
+            if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
+                float mx = sacc[0][qb][0];
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
+                mx = pair_max(mx) * c;
+                const float mnew = fmaxf(mx, mref[qb]);
                 const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
                 mref[qb] = mnew;
                 lsum[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
+                probs();
             }
-            const float nm = -mref[qb];
-            float ls = 0.f;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
-                        ls += p[e];
-                    }
-                    u32x4 pk;
-                    pk[0] = pack_bf16x2(p[0], p[1]);
-                    pk[1] = pack_bf16x2(p[2], p[3]);
-                    pk[2] = pack_bf16x2(p[4], p[5]);
-                    pk[3] = pack_bf16x2(p[6], p[7]);
-                    pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
-                }
             lsum[qb] += ls;
         }
 

@@ -14,7 +14,8 @@ import torch
 
 import oracle
 import spacetime_attention_amd as vd
-from synthetic_inputs import CROSS_WORKLOADS, WORKLOADS, CrossWorkload, draw, sample_rows, small_grid
+from synthetic_inputs import (CROSS_WORKLOADS, WORKLOADS, CrossWorkload, bf16_bits, bf16_to_f32, draw,
+                              sample_rows, small_grid)
 from tests.parity_util import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -70,6 +71,26 @@ def test_peaky_bf16(mode):
     got = to_host(PASSES[mode](q, k, v, grid))
     ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode)
     assert_close(got, ref, "bf16", f"peaky/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial"])
+def test_rising_logits_bf16(mode):
+    # Key norms ramp up 30x along the token order, so the largest score keeps
+    # growing from one key tile to the next by far more than the kernel lets
+    # its reference maximum lag: the reference is raised on many tiles.
+    grid = (4, 10, 25)
+    _announce(f"rising logits bf16 {mode} grid={grid}")
+    w = small_grid("rising", 1, *grid, 2, 128, "bf16", seed=17)
+    d = w.draw_qkv()
+    ramp = (1.0 + 30.0 * np.arange(w.N, dtype=np.float32) / w.N)[None, :, None, None]
+    kb = bf16_bits(d["k"].f32 * ramp)
+    k_f32 = bf16_to_f32(kb).reshape(d["k"].f32.shape)
+    q = to_dev(d["q"])
+    k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).cuda()
+    v = to_dev(d["v"])
+    got = to_host(PASSES[mode](q, k, v, grid))
+    ref = oracle.attention(d["q"].f32, k_f32, d["v"].f32, grid, mode)
+    assert_close(got, ref, "bf16", f"rising/{mode}")
 
 
 def test_single_key_sets_are_exact():
