@@ -64,6 +64,9 @@ def _load():
         lib.oracle_patchify.restype = i
         lib.oracle_rope3d.argtypes = [dp, dp] + [i] * 9 + [ctypes.c_double]
         lib.oracle_rope3d.restype = i
+        lib.oracle_rope3d_rows.argtypes = [dp, dp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + [i] * 9 + [
+            ctypes.c_double]
+        lib.oracle_rope3d_rows.restype = i
         lib.oracle_attention.argtypes = [dp, dp, dp, dp] + [i] * 6 + [ctypes.c_double, i,
                                                                       ctypes.POINTER(ctypes.c_int64),
                                                                       ctypes.c_int64]
@@ -136,6 +139,60 @@ def rope3d(x, grid: Tuple[int, int, int], split: Sequence[int], theta: float = 1
     _check(_load().oracle_rope3d(_ptr(x), _ptr(y), B, T, Hp, Wp, heads, D,
                                  int(split[0]), int(split[1]), int(split[2]), float(theta)))
     return y
+
+
+def rope3d_rows(x, grid: Tuple[int, int, int], rows, split: Sequence[int], theta: float = 10000.0) -> np.ndarray:
+    """3D RoPE on x: (B, R, heads, D) whose row r is grid token rows[r]."""
+    x = _f64(x)
+    B, R, heads, D = x.shape
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if rows.shape != (R,):
+        raise OracleError("one token index per row")
+    T, Hp, Wp = grid
+    y = np.empty_like(x)
+    _check(_load().oracle_rope3d_rows(_ptr(x), _ptr(y), rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), R,
+                                      B, T, Hp, Wp, heads, D, int(split[0]), int(split[1]), int(split[2]),
+                                      float(theta)))
+    return y
+
+
+def rmsnorm(x, gamma, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * gamma."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(gamma)
+
+
+def qkv_proj(x, w, bias, gamma_q, gamma_k, grid: Tuple[int, int, int], heads: int, head_dim: int,
+             split: Optional[Sequence[int]] = None, theta: float = 10000.0, eps: float = 1e-6,
+             rows: Optional[np.ndarray] = None):
+    """The attention input of a DiT block ("How AI Generates Video ...",
+    section 5, attn1): tokens x (B, N, dim) projected by the fused weight
+    w (3*dim, dim) (+ bias (3*dim,)) into Q, K and V of heads x head_dim;
+    Q and K each RMS-normalised over every head's head_dim values with
+    gains gamma_q / gamma_k (dim,) (None: no normalisation), then rotated
+    by 3D RoPE when a split is given. Returns q, k, v (B, R, heads, D) for
+    the token rows ``rows`` (default: all N)."""
+    x, w = _f64(x), _f64(w)
+    B, N, dim = x.shape
+    T, Hp, Wp = grid
+    if N != T * Hp * Wp or dim != heads * head_dim or w.shape != (3 * dim, dim):
+        raise OracleError("shapes do not match")
+    if rows is None:
+        rows = np.arange(N, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    y = x[:, rows] @ w.T
+    if bias is not None:
+        y = y + _f64(bias)
+    R = rows.size
+    q, k, v = (y[..., i * dim:(i + 1) * dim].reshape(B, R, heads, head_dim) for i in range(3))
+    out = []
+    for t, g in ((q, gamma_q), (k, gamma_k)):
+        if g is not None:
+            t = rmsnorm(t, _f64(g).reshape(heads, head_dim), eps)
+        if split is not None:
+            t = rope3d_rows(t, grid, rows, split, theta)
+        out.append(t)
+    return out[0], out[1], np.ascontiguousarray(v)
 
 
 def attention(q, k, v, grid: Tuple[int, int, int], mode: str = "full",

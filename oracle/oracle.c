@@ -97,6 +97,29 @@ int oracle_patchify(const double *x, const double *w, const double *bias, double
  * ("Troubleshooting") makes a split that does not sum to D an error.
  * Applied to every head of every token; y must not overlap x.
  * ------------------------------------------------------------------------ */
+/* Rotate every head of one token at grid position pos = (t, h, w). */
+static void rope_token(const double *x, double *y, const int pos[3], int heads, int D, const int width[3],
+                       double theta)
+{
+    for (int hd = 0; hd < heads; ++hd) {
+        const int64_t base = (int64_t)hd * D;
+        int off = 0;
+        for (int a = 0; a < 3; ++a) {
+            for (int j = 0; j < width[a] / 2; ++j) {
+                const double freq = pow(theta, -2.0 * (double)j / (double)width[a]);
+                const double ang = (double)pos[a] * freq;
+                const double c = cos(ang), s = sin(ang);
+                const double re = x[base + off + 2 * j];
+                const double im = x[base + off + 2 * j + 1];
+                /* (re + i*im) * (c + i*s) */
+                y[base + off + 2 * j] = re * c - im * s;
+                y[base + off + 2 * j + 1] = re * s + im * c;
+            }
+            off += width[a];
+        }
+    }
+}
+
 int oracle_rope3d(const double *x, double *y, int B, int T, int Hp, int Wp, int heads, int D,
                   int d_t, int d_h, int d_w, double theta)
 {
@@ -105,29 +128,38 @@ int oracle_rope3d(const double *x, double *y, int B, int T, int Hp, int Wp, int 
     if (d_t < 0 || d_h < 0 || d_w < 0 || d_t + d_h + d_w != D || (d_t % 2) || (d_h % 2) || (d_w % 2))
         return ORACLE_E_ROPE_SPLIT;
     const int64_t N = (int64_t)T * Hp * Wp;
+    const int width[3] = {d_t, d_h, d_w};
 
     #pragma omp parallel for schedule(static)
     for (int64_t bn = 0; bn < (int64_t)B * N; ++bn) {
         const int64_t n = bn % N;
         const int pos[3] = {(int)(n / ((int64_t)Hp * Wp)), (int)((n / Wp) % Hp), (int)(n % Wp)};
-        const int width[3] = {d_t, d_h, d_w};
-        for (int hd = 0; hd < heads; ++hd) {
-            const int64_t base = (bn * heads + hd) * D;
-            int off = 0;
-            for (int a = 0; a < 3; ++a) {
-                for (int j = 0; j < width[a] / 2; ++j) {
-                    const double freq = pow(theta, -2.0 * (double)j / (double)width[a]);
-                    const double ang = (double)pos[a] * freq;
-                    const double c = cos(ang), s = sin(ang);
-                    const double re = x[base + off + 2 * j];
-                    const double im = x[base + off + 2 * j + 1];
-                    /* (re + i*im) * (c + i*s) */
-                    y[base + off + 2 * j] = re * c - im * s;
-                    y[base + off + 2 * j + 1] = re * s + im * c;
-                }
-                off += width[a];
-            }
-        }
+        rope_token(x + bn * heads * D, y + bn * heads * D, pos, heads, D, width, theta);
+    }
+    return ORACLE_OK;
+}
+
+/* The same rotation for a list of tokens: row r of x and y ([B][nrows][heads]
+ * [D]) holds token rows[r] of the (T, Hp, Wp) grid, whose indices give the
+ * position. */
+int oracle_rope3d_rows(const double *x, double *y, const int64_t *rows, int64_t nrows, int B, int T, int Hp,
+                       int Wp, int heads, int D, int d_t, int d_h, int d_w, double theta)
+{
+    if (!x || !y || !rows || nrows <= 0 || B <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || heads <= 0 || D <= 0)
+        return ORACLE_E_ARG;
+    if (d_t < 0 || d_h < 0 || d_w < 0 || d_t + d_h + d_w != D || (d_t % 2) || (d_h % 2) || (d_w % 2))
+        return ORACLE_E_ROPE_SPLIT;
+    const int64_t N = (int64_t)T * Hp * Wp;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N)
+            return ORACLE_E_ARG;
+    const int width[3] = {d_t, d_h, d_w};
+
+    #pragma omp parallel for schedule(static)
+    for (int64_t br = 0; br < (int64_t)B * nrows; ++br) {
+        const int64_t n = rows[br % nrows];
+        const int pos[3] = {(int)(n / ((int64_t)Hp * Wp)), (int)((n / Wp) % Hp), (int)(n % Wp)};
+        rope_token(x + br * heads * D, y + br * heads * D, pos, heads, D, width, theta);
     }
     return ORACLE_OK;
 }

@@ -184,6 +184,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
     // This wave's queries, as B operands of S^T = K Q^T.
     const int q0 = qblk * S::BM + wave * 32 * QB;
+    // A wave whose queries all lie past the end of the segment (in the last,
+    // ragged query block) still loads its share of every K/V tile and meets
+    // every barrier, but skips the products and the softmax.
+    const bool busy = q0 < L;
     bf16x8 qop[QB][S::KS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -442,12 +446,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // so the next tile's loads start before this tile's products.
     for (int j = 0; j < ntiles; j += 2) {
         if (j + 1 < ntiles) load_tile((j + 1) * kBN, 1);
-        tile(std::integral_constant<int, 0>{}, j);
+        if (busy) tile(std::integral_constant<int, 0>{}, j);
         wait_vmem();
         __syncthreads();
         if (j + 1 >= ntiles) break;
         if (j + 2 < ntiles) load_tile((j + 2) * kBN, 0);
-        tile(std::integral_constant<int, 1>{}, j + 1);
+        if (busy) tile(std::integral_constant<int, 1>{}, j + 1);
         wait_vmem();
         __syncthreads();
     }

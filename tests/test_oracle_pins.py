@@ -394,3 +394,68 @@ def test_window_special_cases():
     rows = np.array([0, 17, 59], dtype=np.int64)
     np.testing.assert_array_equal(oracle.window_attention(q, k, v, grid, (2, 3, 2), rows=rows),
                                   oracle.window_attention(q, k, v, grid, (2, 3, 2))[:, rows])
+
+
+# ----------------------------------------------------------------------------
+# QKV projection with Q/K RMSNorm and RoPE
+# ----------------------------------------------------------------------------
+
+def test_rope_rows_match_grid_rope():
+    grid = (3, 4, 5)
+    x = RNG.standard_normal((2, 60, 2, 32))
+    rows = np.array([0, 7, 23, 59], dtype=np.int64)
+    full = oracle.rope3d(x, grid, (12, 10, 10))
+    np.testing.assert_array_equal(oracle.rope3d_rows(x[:, rows], grid, rows, (12, 10, 10)), full[:, rows])
+
+
+def test_rmsnorm_matches_torch_and_closed_forms():
+    x = RNG.standard_normal((3, 5, 128))
+    g = RNG.standard_normal(128)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rmsnorm(x, g, 1e-6), ref, rtol=1e-12, atol=1e-13)
+    # Unit gain, eps = 0: the mean square of every output row is exactly 1,
+    # and scaling the input by a positive factor changes nothing.
+    y = oracle.rmsnorm(x, np.ones(128), 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rmsnorm(7.5 * x, np.ones(128), 0.0), y, rtol=1e-13)
+    # A constant row c: every output is sign(c) * |c| / sqrt(c^2 + eps) * gain.
+    c, eps = -0.3, 1e-2
+    np.testing.assert_allclose(oracle.rmsnorm(np.full((1, 8), c), np.arange(1, 9), eps),
+                               [np.arange(1, 9) * c / np.sqrt(c * c + eps)], rtol=1e-14)
+
+
+def test_qkv_proj_matches_torch_linear():
+    grid, heads, D = (2, 3, 4), 2, 32
+    dim = heads * D
+    x = RNG.standard_normal((2, 24, dim))
+    w = 0.02 * RNG.standard_normal((3 * dim, dim))
+    b = 0.1 * RNG.standard_normal(3 * dim)
+    q, k, v = oracle.qkv_proj(x, w, b, None, None, grid, heads, D)
+    lin = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    got = np.concatenate([t.reshape(2, 24, dim) for t in (q, k, v)], axis=-1)
+    np.testing.assert_allclose(got, lin, rtol=1e-12, atol=1e-14)
+
+
+def test_qkv_proj_composition():
+    # Identity blocks: q and k are the normalised (and rotated) tokens, v the
+    # tokens themselves; sampled rows equal the same rows of the whole output.
+    grid, heads, D = (2, 3, 5), 2, 32
+    dim = heads * D
+    x = RNG.standard_normal((1, 30, dim))
+    w = np.concatenate([np.eye(dim)] * 3)
+    gq, gk = RNG.standard_normal(dim), RNG.standard_normal(dim)
+    split = (12, 10, 10)
+    q, k, v = oracle.qkv_proj(x, w, None, gq, gk, grid, heads, D, split, eps=1e-6)
+    xh = x.reshape(1, 30, heads, D)
+    np.testing.assert_array_equal(v, xh)
+    np.testing.assert_allclose(q, oracle.rope3d(oracle.rmsnorm(xh, gq.reshape(heads, D), 1e-6), grid, split),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(k, oracle.rope3d(oracle.rmsnorm(xh, gk.reshape(heads, D), 1e-6), grid, split),
+                               rtol=1e-13, atol=1e-14)
+    rows = np.array([1, 17, 29], dtype=np.int64)
+    for a, b_ in zip(oracle.qkv_proj(x, w, None, gq, gk, grid, heads, D, split, rows=rows), (q, k, v)):
+        np.testing.assert_allclose(a, b_[:, rows], rtol=1e-14, atol=1e-15)
+    # Per-head normalisation: each head of q has mean square 1 before the
+    # rotation (unit gain, eps = 0), and the rotation keeps every pair's norm.
+    q1, _, _ = oracle.qkv_proj(x, w, None, np.ones(dim), np.ones(dim), grid, heads, D, split, eps=0.0)
+    np.testing.assert_allclose(np.mean(q1 * q1, axis=-1), 1.0, rtol=1e-12)
