@@ -15,7 +15,9 @@
  *   vdit_attn_cross     attention from the video tokens to another token set
  *                       (the text prompt);
  *   vdit_attn_window    the same, with keys limited to the query's own
- *                       non-overlapping wt x wh x ww spacetime window.
+ *                       non-overlapping wt x wh x ww spacetime window;
+ *   vdit_qkv_proj       the attention input: tokens projected to Q, K, V,
+ *                       with per-head RMSNorm and 3D RoPE on Q and K.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -217,6 +219,40 @@ vdit_status_t vdit_attn_window(const void *q, const void *k, const void *v, void
                                int B, int heads, int T, int Hp, int Wp, int head_dim,
                                int wt, int wh, int ww, float scale, vdit_dtype_t dtype,
                                void *stream);
+
+/*
+ * vdit_qkv_proj — the projection in front of a block's self-attention.
+ *
+ * "How AI Generates Video ...", section 5 (attn1): the tokens are projected
+ * into heads of Queries, Keys and Values, RMSNorm is applied to Q and K, and
+ * Q and K are rotated with the 3D factorised RoPE of section 4. Readings
+ * taken here: one fused weight W [3*dim][dim] (nn.Linear layout [out][in];
+ * rows 0..dim-1 produce Q, dim..2*dim-1 K, 2*dim..3*dim-1 V), dim =
+ * heads*head_dim; the RMSNorm statistic is taken over each head's head_dim
+ * values (the same vectors RoPE then rotates), with a per-channel gain:
+ *   y[m][c]   = bias[c] + sum_j W[c][j] * x[m][j]
+ *   Q[m][h][d] = RoPE_m( y_q[m][h][d] / sqrt(mean_d' y_q[m][h][d']^2 + eps)
+ *                        * gamma_q[h*head_dim + d] )           (K alike)
+ *   V[m][h][d] = y_v[m][h][d]
+ * with RoPE as vdit_rope3d at token m's grid position (t, h, w).
+ * 2*M*3*dim*dim FLOP, M = B*T*Hp*Wp.
+ *
+ * x        : [B, N, dim] tokens (vdit_patchify's output), N = T*Hp*Wp.
+ * w        : [3*dim, dim]; bias: [3*dim] or NULL.
+ * gamma_q, gamma_k : [dim] gains, or NULL to leave that tensor unnormalised.
+ * q, k, v  : [B, N, heads, head_dim] outputs; they may not overlap the inputs
+ *            or each other (VDIT_E_ALIAS).
+ * d_t, d_h, d_w, theta : RoPE split and base as vdit_rope3d; all three zero
+ *            disables the rotation.
+ * eps      : RMSNorm epsilon (>= 0).
+ * Limits   : VDIT_BF16: head_dim 128, dim a multiple of 128, x and w each
+ *            below 2 GiB (else VDIT_E_HEAD_DIM / VDIT_E_SHAPE); VDIT_F32:
+ *            head_dim <= 256, for small workloads. Pointers 16-byte aligned.
+ */
+vdit_status_t vdit_qkv_proj(const void *x, const void *w, const void *bias, const void *gamma_q,
+                            const void *gamma_k, void *q, void *k, void *v, int B, int T, int Hp,
+                            int Wp, int heads, int head_dim, int d_t, int d_h, int d_w, float theta,
+                            float eps, vdit_dtype_t dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,8 @@ BF16, F32 = 0, 1
 STATUS = ["VDIT_OK", "VDIT_E_NULL", "VDIT_E_SHAPE", "VDIT_E_HEAD_DIM", "VDIT_E_ROPE_SPLIT",
           "VDIT_E_ALIGN", "VDIT_E_ALIAS", "VDIT_E_DTYPE", "VDIT_E_LAUNCH"]
 EXPORTS = ("vdit_status_str", "vdit_patchify", "vdit_rope3d", "vdit_attn_full",
-           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross", "vdit_attn_window")
+           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross", "vdit_attn_window",
+           "vdit_qkv_proj")
 
 
 class VditError(RuntimeError):
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vdit_attn_cross.restype = i
     lib.vdit_attn_window.argtypes = [vp, vp, vp, vp] + [i] * 9 + [f, i, vp]
     lib.vdit_attn_window.restype = i
+    lib.vdit_qkv_proj.argtypes = [vp] * 8 + [i] * 9 + [f, f, i, vp]
+    lib.vdit_qkv_proj.restype = i
     _lib = lib
     return lib
 
@@ -219,6 +222,31 @@ def attn_window(q, k, v, grid, window, scale: float = 0.0, out=None) -> torch.Te
     _check(lib.vdit_attn_window(_dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
                                 B, heads, T, Hp, Wp, D, wt, wh, ww, float(scale), _dtype_code(q), _stream(q)))
     return out
+
+
+def qkv_proj(x, w, bias=None, gamma_q=None, gamma_k=None, *, grid, heads: int, head_dim: int,
+             split: Optional[Sequence[int]] = None, theta: float = 10000.0, eps: float = 1e-6, out=None):
+    """Tokens ``x [B, N, dim]`` -> (q, k, v) ``[B, N, heads, head_dim]``: the
+    fused projection ``w [3*dim, dim]`` (+ ``bias``), per-head RMSNorm of Q
+    and K with gains ``gamma_q`` / ``gamma_k`` (None: not normalised), and 3D
+    RoPE on Q and K when ``split`` is given."""
+    B, N, dim = x.shape
+    T, Hp, Wp = grid
+    if N != T * Hp * Wp or dim != heads * head_dim or tuple(w.shape) != (3 * dim, dim):
+        raise ValueError("shapes do not match")
+    shape = (B, N, heads, head_dim)
+    if out is None:
+        out = tuple(torch.empty(shape, dtype=x.dtype, device=x.device) for _ in range(3))
+    q, k, v = out
+    d_t, d_h, d_w = (int(a) for a in split) if split is not None else (0, 0, 0)
+    lib = load_library()
+    dt = x.dtype
+    opt = lambda t, n: None if t is None else _dev(t, n, dt)
+    _check(lib.vdit_qkv_proj(_dev(x, "x"), _dev(w, "w", dt), opt(bias, "bias"), opt(gamma_q, "gamma_q"),
+                             opt(gamma_k, "gamma_k"), _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt),
+                             B, T, Hp, Wp, heads, head_dim, d_t, d_h, d_w, float(theta), float(eps),
+                             _dtype_code(x), _stream(x)))
+    return q, k, v
 
 
 def divided(x: torch.Tensor, grid, order=("spatial", "temporal"), split: Optional[Sequence[int]] = None,

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvdit.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["attn_flash.hip", "attn_temporal.hip", "attn_f32.hip", "patchify.hip", "rope3d.hip", "vdit_abi.hip"]
+SOURCES = ["attn_flash.hip", "attn_temporal.hip", "attn_f32.hip", "patchify.hip", "rope3d.hip", "qkv_proj.hip",
+           "vdit_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

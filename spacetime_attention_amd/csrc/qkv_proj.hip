@@ -1,0 +1,333 @@
+// QKV projection of a DiT block's attention input (bf16, gfx950), with the
+// per-head RMSNorm of Q and K and their 3D rotation fused into the epilogue.
+//
+// "How AI Generates Video: Inside Sora and Wan2.1 on a Real GPU", section 5
+// (attn1): the block projects its tokens into heads of 128-wide queries, keys
+// and values, applies RMSNorm to Q and K, and rotates Q and K with the
+// [44, 42, 42] factorised RoPE of section 4. With a fused weight W
+// [3*dim][dim] (rows 0..dim-1 make Q, then K, then V) and tokens x [M][dim]:
+//   y[m][c] = bias[c] + sum_k W[c][k] x[m][k]
+//   Q, K: each head's head_dim values scaled by 1/sqrt(mean(y^2) + eps) and
+//         by the per-channel gain, then rotated by the token's (t, h, w);
+//   V:    y as is.
+//
+// The product is formed transposed, out^T = W x^T, on
+// v_mfma_f32_32x32x16_bf16: the A operand is a 32-channel block of W, the B
+// operand a 32-token block of x, both K-contiguous rows read from LDS. In the
+// result a lane owns one token and 16 channels per block; over a head's four
+// blocks, lanes l and l^32 together hold the token's 128 channels, so the
+// head's mean square is a register sum plus one v_permlane32_swap, and each
+// RoPE pair (2j, 2j+1) sits in one lane's consecutive registers.
+//
+// Work layout: a workgroup (4 wavefronts, one per SIMD) owns a 256-channel x
+// 256-token tile; a wavefront owns 128 channels (one head) x 128 tokens, i.e.
+// 4 x 4 blocks and 16 accumulators. K advances in stages of 64: W and x
+// tiles of [256][64] bf16 are filled by buffer loads that write LDS directly
+// and are double-buffered; a chunk-XOR swizzle keeps the operand reads
+// (32 rows, one 16-byte chunk each) free of bank conflicts. Rows past the end
+// of W or x read as zero through the buffer descriptors' sizes.
+#include "vdit_internal.h"
+
+#include <type_traits>
+
+namespace vdit {
+namespace {
+
+constexpr int kTileC = 256;  // channels per workgroup
+constexpr int kTileT = 256;  // tokens per workgroup
+constexpr int kBK = 64;      // k per LDS stage
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kBK * 2;                  // 128 bytes of one tile row
+constexpr int kTileBytes = kTileC * kRowBytes;      // 32 KB (W or x tile)
+constexpr int kStageBytes = 2 * kTileBytes;         // W tile then x tile
+constexpr int kLdsBytes = 2 * kStageBytes;          // two stages: 128 KB
+constexpr int kLoads = kTileBytes / 1024 / (kThreads / 64);  // 1 KB loads per wave per tile
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+constexpr int kBufferFlags = 0x00020000;
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Physical 16-byte chunk of logical chunk c in tile row r: rows are 128
+// bytes, two per 256-byte bank period, so XOR with (r/2) % 8 spreads the 16
+// rows one b128 read pass touches over all banks.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w, const uint16_t *__restrict__ bias,
+    const uint16_t *__restrict__ gq, const uint16_t *__restrict__ gk, uint16_t *__restrict__ q,
+    uint16_t *__restrict__ k, uint16_t *__restrict__ v, QkvGeom g, QkvRope rope)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    lds_u8 *lds = (lds_u8 *)dyn_lds;
+    const int dim = g.dim;
+    const int nct = (3 * dim + kTileC - 1) / kTileC;
+    const int ntt = (g.M + kTileT - 1) / kTileT;
+    const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)(nct * ntt));
+    const int ct = (int)(id % nct), tt = (int)(id / nct);
+    const int c0 = ct * kTileC, t0 = tt * kTileT;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, col = lane & 31;
+    const int wc = wave & 1, wt = wave >> 1;  // channel half, token half of the tile
+
+    // Buffer descriptors from the tile's first W row and first x row; the
+    // sizes end at the last row of each matrix.
+    const uint32_t rowb = (uint32_t)dim * 2;
+    const int nrec_w = (int)((int64_t)(3 * dim - c0) * rowb);
+    const int nrec_x = (int)((int64_t)(g.M - t0) * rowb);
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(w + (int64_t)c0 * dim), 0, nrec_w, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(x + (int64_t)t0 * dim), 0, nrec_x, kBufferFlags);
+    // Load i of this wave fills tile rows 8*(wave*kLoads + i) + lane/8,
+    // physical chunk lane%8, which holds logical chunk (lane%8) ^ swz.
+    uint32_t goff[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const int r = 8 * (wave * kLoads + i) + (lane >> 3);
+        goff[i] = (uint32_t)r * rowb + (uint32_t)swz(r, lane & 7) * 16;
+    }
+    auto load_stage = [&](int kt, int st) {
+        lds_u8 *wb = lds + st * kStageBytes;
+        lds_u8 *xb = wb + kTileBytes;
+        const uint32_t so = (uint32_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void *)(wb + (wave * kLoads + i) * 1024), 16,
+                                                     goff[i], so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void *)(xb + (wave * kLoads + i) * 1024), 16,
+                                                     goff[i], so, 0, 0);
+        }
+    };
+
+    // Operand read offsets for k-step 0 of stage 0: W row wc*128 + col (+32
+    // per channel block), x row wt*128 + col (+32 per token block); the
+    // swizzle depends on the row only through col.
+    uint32_t aofs[4], bofs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        aofs[ks] = (uint32_t)((wc * 128 + col) * kRowBytes + swz(col, 2 * ks + half) * 16);
+        bofs[ks] = (uint32_t)(kTileBytes + (wt * 128 + col) * kRowBytes + swz(col, 2 * ks + half) * 16);
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = (f32x16){};
+
+    const int nk = dim / kBK;
+    auto stage = [&](auto stc) {
+        constexpr uint32_t S0 = decltype(stc)::value * kStageBytes;
+        bf16x8 a[2][4], b[2][4];
+        auto rd = [&](int ks, int slot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[slot][i] = *(const lds_bf16x8 *)(lds + aofs[ks] + (S0 + i * 32 * kRowBytes));
+                b[slot][i] = *(const lds_bf16x8 *)(lds + bofs[ks] + (S0 + i * 32 * kRowBytes));
+            }
+        };
+        rd(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            if (ks + 1 < 4) rd(ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][cb], b[ks & 1][tb],
+                                                                         acc[cb][tb], 0, 0, 0);
+        }
+    };
+
+    // Stages alternate between the two LDS buffers; the loop takes them in
+    // pairs so the buffer is a compile-time constant, and an odd last stage
+    // (already loaded into buffer 0) follows it.
+    load_stage(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        load_stage(kt + 1, 1);
+        stage(std::integral_constant<int, 0>{});
+        wait_vmem();
+        __syncthreads();
+        if (kt + 2 < nk) load_stage(kt + 2, 0);
+        stage(std::integral_constant<int, 1>{});
+        wait_vmem();
+        __syncthreads();
+    }
+    if (kt < nk) stage(std::integral_constant<int, 0>{});
+
+    // Epilogue: this wave's 128 channels are one head of one of Q, K, V.
+    const int cw = c0 + wc * 128;
+    if (cw >= 3 * dim) return;
+    const int which = cw / dim;             // 0 Q, 1 K, 2 V
+    const int hc = cw - which * dim;        // first channel of the head within its tensor
+    uint16_t *out = which == 0 ? q : (which == 1 ? k : v);
+    const uint16_t *gain = which == 0 ? gq : (which == 1 ? gk : nullptr);
+    const bool rot = which < 2 && rope.on;
+    const int HW = g.Hp * g.Wp;
+    // Lane channels within the head: cb*32 + 8*(r/4) + 4*half + r%4. Bias
+    // and gain are read per channel block (they stay in L1), and every step
+    // works in place on the accumulators.
+    auto load4 = [&](const uint16_t *p, int cb, int r4, float dflt, float out4[4]) {
+        if (!p) {
+            out4[0] = out4[1] = out4[2] = out4[3] = dflt;
+            return;
+        }
+        const u32x2 u = *(const u32x2 *)(p + cb * 32 + 8 * r4 + 4 * half);
+        out4[0] = bf16_bits_to_f32(u[0] & 0xffffu);
+        out4[1] = bf16_bits_to_f32(u[0] >> 16);
+        out4[2] = bf16_bits_to_f32(u[1] & 0xffffu);
+        out4[3] = bf16_bits_to_f32(u[1] >> 16);
+    };
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const int m = t0 + wt * 128 + tb * 32 + col;  // token row (batch-major)
+        float ss = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float b4[4];
+                load4(bias ? bias + cw : nullptr, cb, r4, 0.f, b4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = acc[cb][tb][4 * r4 + e] + b4[e];
+                    acc[cb][tb][4 * r4 + e] = y;
+                    ss = fmaf(y, y, ss);
+                }
+            }
+        if (gain) {
+            const float sc = __builtin_amdgcn_rsqf(pair_sum(ss) * (1.0f / 128.0f) + g.eps);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    float g4[4];
+                    load4(gain + hc, cb, r4, 1.f, g4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[cb][tb][4 * r4 + e] *= sc * g4[e];
+                }
+        }
+        if (rot) {
+            const int n = m % g.N;
+            const float pos[3] = {(float)(n / HW), (float)((n / g.Wp) % g.Hp), (float)(n % g.Wp)};
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int pr = (cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3)) >> 1;  // pair index
+                    // Angle in revolutions, reduced to [0, 1) for v_sin/v_cos.
+                    const float rev = __builtin_amdgcn_fractf(pos[rope.axis[pr]] * rope.freq_rev[pr]);
+                    const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                    const float re = acc[cb][tb][r], im = acc[cb][tb][r + 1];
+                    acc[cb][tb][r] = re * cs - im * sn;
+                    acc[cb][tb][r + 1] = re * sn + im * cs;
+                }
+        }
+        if (m < g.M) {
+            uint16_t *op = out + (int64_t)m * dim + hc;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    u32x2 st;
+                    st[0] = pack_bf16x2(acc[cb][tb][4 * r4 + 0], acc[cb][tb][4 * r4 + 1]);
+                    st[1] = pack_bf16x2(acc[cb][tb][4 * r4 + 2], acc[cb][tb][4 * r4 + 3]);
+                    *(u32x2 *)(op + cb * 32 + 8 * r4 + 4 * half) = st;
+                }
+        }
+    }
+#endif
+}
+
+// fp32: one thread per (token, tensor, head), fp32 dot products, fp64
+// angles; for small workloads checked against fp64 at 1e-5.
+__global__ __launch_bounds__(128) void qkv_proj_f32(const float *__restrict__ x, const float *__restrict__ w,
+                                                    const float *__restrict__ bias, const float *__restrict__ gq,
+                                                    const float *__restrict__ gk, float *__restrict__ q,
+                                                    float *__restrict__ k, float *__restrict__ v, QkvGeom g,
+                                                    RopeTable tab, int rope_on)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int heads = g.dim / g.D;
+    if (idx >= (int64_t)g.M * 3 * heads) return;
+    const int hd = (int)(idx % heads);
+    const int which = (int)((idx / heads) % 3);
+    const int64_t m = idx / (3 * heads);
+    const float *xr = x + m * g.dim;
+    float y[256];
+    const int D = g.D;
+    for (int d = 0; d < D; ++d) {
+        const int c = which * g.dim + hd * D + d;
+        const float *wr = w + (int64_t)c * g.dim;
+        float s = 0.f;
+        for (int kk = 0; kk < g.dim; ++kk) s = fmaf(wr[kk], xr[kk], s);
+        y[d] = s + (bias ? bias[c] : 0.f);
+    }
+    const float *gain = which == 0 ? gq : (which == 1 ? gk : nullptr);
+    if (gain) {
+        float ss = 0.f;
+        for (int d = 0; d < D; ++d) ss = fmaf(y[d], y[d], ss);
+        const float sc = 1.0f / sqrtf(ss / (float)D + g.eps);
+        for (int d = 0; d < D; ++d) y[d] = y[d] * sc * gain[hd * D + d];
+    }
+    if (which < 2 && rope_on) {
+        const int n = (int)(m % g.N);
+        const int pos[3] = {n / (g.Hp * g.Wp), (n / g.Wp) % g.Hp, n % g.Wp};
+        for (int j = 0; j < D / 2; ++j) {
+            double ang = (double)pos[tab.axis[j]] * tab.freq[j];
+            ang -= 6.283185307179586476925286766559 * rint(ang * 0.15915494309189533576888376337251);
+            float sn, cs;
+            sincosf((float)ang, &sn, &cs);
+            const float re = y[2 * j], im = y[2 * j + 1];
+            y[2 * j] = re * cs - im * sn;
+            y[2 * j + 1] = re * sn + im * cs;
+        }
+    }
+    float *out = which == 0 ? q : (which == 1 ? k : v);
+    for (int d = 0; d < D; ++d) out[m * g.dim + hd * D + d] = y[d];
+}
+
+}  // namespace
+
+hipError_t launch_qkv_proj_bf16(const void *x, const void *w, const void *bias, const void *gq, const void *gk,
+                                void *q, void *k, void *v, const QkvGeom &g, const QkvRope &rope, hipStream_t s) {
+    const int64_t nct = (3 * (int64_t)g.dim + kTileC - 1) / kTileC;
+    const int64_t ntt = ((int64_t)g.M + kTileT - 1) / kTileT;
+    const int64_t grid = nct * ntt;
+    if (grid <= 0 || grid > UINT32_MAX) return hipErrorInvalidConfiguration;
+    hipError_t e = hipFuncSetAttribute((const void *)qkv_proj_bf16, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(qkv_proj_bf16, dim3((uint32_t)grid), dim3(kThreads), kLdsBytes, s, (const uint16_t *)x,
+                       (const uint16_t *)w, (const uint16_t *)bias, (const uint16_t *)gq, (const uint16_t *)gk,
+                       (uint16_t *)q, (uint16_t *)k, (uint16_t *)v, g, rope);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_proj_f32(const float *x, const float *w, const float *bias, const float *gq, const float *gk,
+                               float *q, float *k, float *v, const QkvGeom &g, const RopeTable &tab, int rope_on,
+                               hipStream_t s) {
+    const int64_t n = (int64_t)g.M * 3 * (g.dim / g.D);
+    const int64_t blocks = (n + 127) / 128;
+    if (blocks <= 0 || blocks > UINT32_MAX) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(qkv_proj_f32, dim3((uint32_t)blocks), dim3(128), 0, s, x, w, bias, gq, gk, q, k, v, g, tab,
+                       rope_on);
+    return hipGetLastError();
+}
+
+}  // namespace vdit

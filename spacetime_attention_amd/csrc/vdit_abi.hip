@@ -168,6 +168,78 @@ vdit_status_t vdit_attn_window(const void *q, const void *k, const void *v, void
     return launch_status(launch_window_bf16(q, k, v, o, B, heads, D, g, (float)((double)s * kLog2e), st));
 }
 
+vdit_status_t vdit_qkv_proj(const void *x, const void *w, const void *bias, const void *gamma_q,
+                            const void *gamma_k, void *q, void *k, void *v, int B, int T, int Hp, int Wp, int heads,
+                            int head_dim, int d_t, int d_h, int d_w, float theta, float eps, vdit_dtype_t dtype,
+                            void *stream) {
+    if (!x || !w || !q || !k || !v) return VDIT_E_NULL;
+    if (dtype != VDIT_BF16 && dtype != VDIT_F32) return VDIT_E_DTYPE;
+    if (B <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || heads <= 0 || head_dim <= 0) return VDIT_E_SHAPE;
+    const int D = head_dim;
+    if (dtype == VDIT_BF16 && D != 128) return VDIT_E_HEAD_DIM;
+    if (dtype == VDIT_F32 && (D > 256 || D % 2)) return VDIT_E_HEAD_DIM;
+    const bool rope_on = d_t != 0 || d_h != 0 || d_w != 0;
+    if (rope_on && (d_t < 0 || d_h < 0 || d_w < 0 || (d_t & 1) || (d_h & 1) || (d_w & 1) ||
+                    (int64_t)d_t + d_h + d_w != D))
+        return VDIT_E_ROPE_SPLIT;
+    if (rope_on && (!(theta > 0.f) || !std::isfinite(theta))) return VDIT_E_SHAPE;
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return VDIT_E_SHAPE;
+    uint64_t n_tok = 1, dim = 1;
+    if (!mul_ok(n_tok, B) || !mul_ok(n_tok, T) || !mul_ok(n_tok, Hp) || !mul_ok(n_tok, Wp)) return VDIT_E_SHAPE;
+    if (!mul_ok(dim, heads) || !mul_ok(dim, D)) return VDIT_E_SHAPE;
+    if (n_tok > (uint64_t)INT32_MAX || dim * 3 > (uint64_t)INT32_MAX) return VDIT_E_SHAPE;
+    uint64_t xel = n_tok, wel = dim * 3;
+    if (!mul_ok(xel, (int64_t)dim) || !mul_ok(wel, (int64_t)dim)) return VDIT_E_SHAPE;
+    const uint64_t es = (uint64_t)esize(dtype);
+    if (dtype == VDIT_BF16) {
+        // K advances 64 at a time and the epilogue takes whole heads; the
+        // buffer descriptors' byte ranges are signed 32-bit values.
+        if (dim % 128) return VDIT_E_SHAPE;
+        if (xel * 2 >= (uint64_t(1) << 31) || wel * 2 >= (uint64_t(1) << 31)) return VDIT_E_SHAPE;
+    }
+    if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        (bias && !aligned16(bias)) || (gamma_q && !aligned16(gamma_q)) || (gamma_k && !aligned16(gamma_k)))
+        return VDIT_E_ALIGN;
+    const uint64_t ob = xel * es;
+    const void *outs[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], ob, x, xel * es) || overlap(outs[i], ob, w, wel * es) ||
+            (bias && overlap(outs[i], ob, bias, dim * 3 * es)) || (gamma_q && overlap(outs[i], ob, gamma_q, dim * es)) ||
+            (gamma_k && overlap(outs[i], ob, gamma_k, dim * es)))
+            return VDIT_E_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], ob, outs[j], ob)) return VDIT_E_ALIAS;
+    }
+    QkvGeom g{(int)n_tok, T * Hp * Wp, Hp, Wp, (int)dim, D, eps};
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int width[3] = {d_t, d_h, d_w};
+    if (dtype == VDIT_F32) {
+        RopeTable tab{};
+        int j = 0;
+        if (rope_on)
+            for (int a = 0; a < 3; ++a)
+                for (int jj = 0; jj < width[a] / 2; ++jj, ++j) {
+                    tab.axis[j] = (unsigned char)a;
+                    tab.freq[j] = std::pow((double)theta, -2.0 * jj / (double)width[a]);
+                }
+        return launch_status(launch_qkv_proj_f32((const float *)x, (const float *)w, (const float *)bias,
+                                                 (const float *)gamma_q, (const float *)gamma_k, (float *)q,
+                                                 (float *)k, (float *)v, g, tab, rope_on ? 1 : 0, st));
+    }
+    QkvRope rope{};
+    rope.on = rope_on ? 1 : 0;
+    if (rope_on) {
+        int j = 0;
+        for (int a = 0; a < 3; ++a)
+            for (int jj = 0; jj < width[a] / 2; ++jj, ++j) {
+                rope.axis[j] = (unsigned char)a;
+                rope.freq_rev[j] = (float)(std::pow((double)theta, -2.0 * jj / (double)width[a]) /
+                                           6.283185307179586476925286766559);
+            }
+    }
+    return launch_status(launch_qkv_proj_bf16(x, w, bias, gamma_q, gamma_k, q, k, v, g, rope, st));
+}
+
 vdit_status_t vdit_patchify(const void *latent, const void *weight, const void *bias, void *tokens, int B, int C,
                             int pt, int ph, int pw, int Tl, int Hl, int Wl, int heads, int T, int Hp, int Wp,
                             int head_dim, vdit_dtype_t dtype, void *stream) {

@@ -100,4 +100,24 @@ hipError_t launch_rope_bf16(const void *x, void *y, int B, int heads, int T, int
 hipError_t launch_rope_f32(const float *x, float *y, int B, int heads, int T, int Hp, int Wp, int D,
                            const RopeTable &tab, hipStream_t s);
 
+// QKV projection: tokens x [M][dim] (M = B*N, batch-major), fused weight
+// [3*dim][dim], outputs [M][dim] each; token m sits at grid index m % N of a
+// (T, Hp, Wp) grid. D is head_dim.
+struct QkvGeom {
+    int M, N, Hp, Wp, dim, D;
+    float eps;
+};
+// Rotation for the bf16 kernel: per pair j (< 64) its axis and frequency in
+// revolutions per grid step (theta^(-2jj/d_a) / (2 pi)); on = 0 disables it.
+struct QkvRope {
+    float freq_rev[64];
+    unsigned char axis[64];
+    int on;
+};
+hipError_t launch_qkv_proj_bf16(const void *x, const void *w, const void *bias, const void *gq, const void *gk,
+                                void *q, void *k, void *v, const QkvGeom &g, const QkvRope &rope, hipStream_t s);
+hipError_t launch_qkv_proj_f32(const float *x, const float *w, const float *bias, const float *gq, const float *gk,
+                               float *q, float *k, float *v, const QkvGeom &g, const RopeTable &tab, int rope_on,
+                               hipStream_t s);
+
 }  // namespace vdit

@@ -218,6 +218,55 @@ CROSS_WORKLOADS: Dict[str, CrossWorkload] = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class QkvWorkload:
+    """The projection in front of self-attention: tokens x [B, N, dim] drawn
+    N(0,1), then the fused weight [3*dim, dim] and bias [3*dim] drawn
+    N(0, weight_std^2), then the Q and K RMSNorm gains [dim] drawn as
+    1 + N(0, weight_std^2), in that order."""
+    name: str
+    B: int
+    T: int
+    Hp: int
+    Wp: int
+    heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+    weight_std: float = 0.02
+    rope_split: Optional[Tuple[int, int, int]] = None
+
+    @property
+    def N(self) -> int:
+        return self.T * self.Hp * self.Wp
+
+    @property
+    def dim(self) -> int:
+        return self.heads * self.head_dim
+
+    def draw(self) -> Dict[str, Drawn]:
+        dim, s = self.dim, self.weight_std
+        d = draw(self.seed, [("x", (self.B, self.N, dim), 1.0), ("w", (3 * dim, dim), s), ("bias", (3 * dim,), s),
+                             ("gq", (dim,), s), ("gk", (dim,), s)], "f32")
+        out: Dict[str, Drawn] = {}
+        for name, t in d.items():
+            v = t.f32 + np.float32(1.0) if name in ("gq", "gk") else t.f32
+            if self.dtype == "bf16":
+                bits = bf16_bits(v)
+                out[name] = Drawn(name, bf16_to_f32(bits).reshape(v.shape), bits.reshape(v.shape))
+            else:
+                out[name] = Drawn(name, v, None)
+        return out
+
+
+QKV_WORKLOADS: Dict[str, QkvWorkload] = {
+    # Wan 1.3B-shaped attn1 input at 480p: 32,760 tokens of width 1,536 ->
+    # Q, K, V of 12 heads x 128, per-head RMSNorm on Q and K, RoPE [44,42,42].
+    "qkv_480p": QkvWorkload("qkv_480p", B=1, T=21, Hp=30, Wp=52, heads=12, head_dim=128, dtype="bf16", seed=7,
+                            rope_split=(44, 42, 42)),
+}
+
+
 def small_grid(name: str, B: int, T: int, Hp: int, Wp: int, heads: int, head_dim: int,
                dtype: str, seed: int, **kw) -> Workload:
     """An ad-hoc workload for parity and edge cases."""

@@ -132,3 +132,26 @@ def test_window_argument_errors(lib):
     assert call(k=K + 8) == 5
     assert call(o=V + 16) == 6
     assert call(dt=5) == 7
+
+
+def test_qkv_proj_argument_errors(lib):
+    f = lib.vdit_qkv_proj
+    G = 5 * P << 8
+
+    def call(x=Q, w=K, b=None, gq=None, gk=None, q=O, k=V + (1 << 24), v=G, B=1, T=2, Hp=3, Wp=4, heads=2, D=128,
+             dt_=44, dh=42, dw=42, theta=10000.0, eps=1e-6, dt=vd.BF16):
+        return f(x, w, b, gq, gk, q, k, v, B, T, Hp, Wp, heads, D, dt_, dh, dw, theta, eps, dt, None)
+
+    assert call(x=None) == 1
+    assert call(v=None) == 1
+    assert call(T=0) == 2
+    assert call(eps=-1.0) == 2
+    assert call(theta=0.0) == 2
+    assert call(D=64, dt_=24, dh=20, dw=20) == 3      # bf16 takes head_dim 128 only
+    assert call(dt=vd.F32, D=300, dt_=100, dh=100, dw=100) == 3
+    assert call(dw=40) == 4                          # split does not sum to head_dim
+    assert call(dt_=0, dh=0, dw=0, w=K + 8) == 5     # an all-zero split (no rotation) passes that check
+    assert call(w=K + 8) == 5
+    assert call(q=Q + 16) == 6                       # output overlaps x
+    assert call(k=O + 64) == 6                       # outputs overlap each other
+    assert call(dt=3) == 7

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import spacetime_attention_amd as vd
-from synthetic_inputs import (CROSS_WORKLOADS, WORKLOADS, CrossWorkload, bf16_bits, bf16_to_f32, draw,
-                              sample_rows, small_grid)
+from synthetic_inputs import (CROSS_WORKLOADS, QKV_WORKLOADS, WORKLOADS, CrossWorkload, QkvWorkload, bf16_bits,
+                              bf16_to_f32, draw, sample_rows, small_grid)
 from tests.parity_util import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -405,3 +405,50 @@ def test_480p_window_sampled(window, stride):
     got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
     ref = oracle.window_attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, window, rows=rows)
     assert_close(got_rows, ref, "bf16", f"480p_window/{window}")
+
+
+# ----------------------------------------------------------------------------
+# QKV projection with per-head Q/K RMSNorm and 3D RoPE
+# ----------------------------------------------------------------------------
+
+QKV_SMALL = [
+    # (name, B, grid, heads, head_dim, dtype, split, bias, norm)
+    ("ragged_tokens", 2, (3, 5, 7), 2, 128, "bf16", (44, 42, 42), True, True),
+    ("odd_heads_no_rope", 1, (2, 4, 9), 3, 128, "bf16", None, False, True),
+    ("multi_tile", 1, (4, 10, 25), 4, 128, "bf16", (44, 42, 42), True, True),
+    ("plain_projection", 1, (1, 16, 16), 2, 128, "bf16", None, True, False),
+    ("tiny_width_f32", 1, (4, 8, 8), 2, 32, "f32", (12, 10, 10), True, True),
+    ("f32_d128", 2, (2, 3, 5), 2, 128, "f32", (44, 42, 42), False, True),
+]
+
+
+def _qkv_case(w, d, split, use_bias, norm, rows=None):
+    dev = {n: to_dev(d[n]) for n in d}
+    grid = (w.T, w.Hp, w.Wp)
+    got = vd.qkv_proj(dev["x"], dev["w"], dev["bias"] if use_bias else None, dev["gq"] if norm else None,
+                      dev["gk"] if norm else None, grid=grid, heads=w.heads, head_dim=w.head_dim, split=split)
+    ref = oracle.qkv_proj(d["x"].f32, d["w"].f32, d["bias"].f32 if use_bias else None,
+                          d["gq"].f32 if norm else None, d["gk"].f32 if norm else None, grid, w.heads, w.head_dim,
+                          split, rows=rows)
+    return got, ref
+
+
+@pytest.mark.parametrize("case", QKV_SMALL, ids=[c[0] for c in QKV_SMALL])
+def test_qkv_proj_small(case):
+    name, B, grid, heads, D, dtype, split, use_bias, norm = case
+    _announce(f"qkv_proj {name} B={B} grid={grid} heads={heads} D={D} {dtype} split={split}")
+    w = QkvWorkload(name, B, *grid, heads, D, dtype, seed=300 + len(name))
+    got, ref = _qkv_case(w, w.draw(), split, use_bias, norm)
+    for t, g, r in zip("qkv", got, ref):
+        assert_close(to_host(g), r, dtype, f"qkv/{name}/{t}")
+
+
+def test_qkv_proj_480p_sampled():
+    w = QKV_WORKLOADS["qkv_480p"]
+    _announce("qkv_proj 480p: [1,32760,1536] x [4608,1536], rows every 61")
+    d = w.draw()
+    rows = sample_rows(w.N, 61, offset=20)
+    got, ref = _qkv_case(w, d, w.rope_split, True, True, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    for t, g, r in zip("qkv", got, ref):
+        assert_close(to_host(g[:, idx]), r, "bf16", f"qkv_480p/{t}")
