@@ -219,7 +219,8 @@ def main():
         "cpu_baseline": None,
     }
 
-    result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch)}
+    result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
+                           "qkv_proj": bench_qkv(vd, torch)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
         result["cpu_baseline"]["gpu_over_cpu"] = per_pass["full"]["tflops"] / result["cpu_baseline"]["value"]
@@ -290,6 +291,36 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def bench_qkv(vd, torch, iters: int = 20):
+    """The projection in front of self-attention, timed on its own after the
+    step: [1,32760,1536] tokens x fused [4608,1536] weight with bias, per-head
+    RMSNorm and RoPE [44,42,42] on Q and K."""
+    from synthetic_inputs import QKV_WORKLOADS
+    w = QKV_WORKLOADS["qkv_480p"]
+    d = w.draw()
+    x, wt, b, gq, gk = (_dev(d[n]) for n in ("x", "w", "bias", "gq", "gk"))
+    grid = (w.T, w.Hp, w.Wp)
+    shape = (w.B, w.N, w.heads, w.head_dim)
+    out = tuple(torch.empty(shape, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+
+    def run():
+        vd.qkv_proj(x, wt, b, gq, gk, grid=grid, heads=w.heads, head_dim=w.head_dim, split=w.rope_split, out=out)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / iters
+    flop = 2.0 * w.B * w.N * 3 * w.dim * w.dim
+    return {"workload": f"x [{w.B},{w.N},{w.dim}] x w [{3 * w.dim},{w.dim}], RMSNorm + RoPE on Q/K",
+            "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 
 def cpu_baseline(df, wf):
