@@ -171,6 +171,10 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     if (kt < nk) stage(std::integral_constant<int, 0>{});
 
     // Epilogue: this wave's 128 channels are one head of one of Q, K, V.
+    // Lane channels within the head: cb*32 + 8*r4 + 4*half + e, e < 4 (the
+    // accumulator register 4*r4 + e of block cb). Every 32-token block is
+    // finished in registers, staged through this wave's own LDS region and
+    // written as whole 256-byte token rows.
     const int cw = c0 + wc * 128;
     if (cw >= 3 * dim) return;
     const int which = cw / dim;             // 0 Q, 1 K, 2 V
@@ -179,35 +183,40 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     const uint16_t *gain = which == 0 ? gq : (which == 1 ? gk : nullptr);
     const bool rot = which < 2 && rope.on;
     const int HW = g.Hp * g.Wp;
-    // Lane channels within the head: cb*32 + 8*(r/4) + 4*half + r%4. Bias
-    // and gain are read per channel block (they stay in L1), and every step
-    // works in place on the accumulators.
-    auto load4 = [&](const uint16_t *p, int cb, int r4, float dflt, float out4[4]) {
-        if (!p) {
-            out4[0] = out4[1] = out4[2] = out4[3] = dflt;
-            return;
+
+    // Bias and gain of the lane's 64 channels as packed bf16 pairs.
+    u32x2 bw[4][4], gw[4][4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int ch = cb * 32 + 8 * r4 + 4 * half;
+            bw[cb][r4] = bias ? *(const u32x2 *)(bias + cw + ch) : (u32x2){0u, 0u};
+            gw[cb][r4] = gain ? *(const u32x2 *)(gain + hc + ch) : (u32x2){0x3f803f80u, 0x3f803f80u};
         }
-        const u32x2 u = *(const u32x2 *)(p + cb * 32 + 8 * r4 + 4 * half);
-        out4[0] = bf16_bits_to_f32(u[0] & 0xffffu);
-        out4[1] = bf16_bits_to_f32(u[0] >> 16);
-        out4[2] = bf16_bits_to_f32(u[1] & 0xffffu);
-        out4[3] = bf16_bits_to_f32(u[1] >> 16);
-    };
+    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+    // RoPE: pair rp of block cb is channel pair p = cb*16 + 4*(rp/2) + rp%2
+    // + 2*half; pairs below rope.b1 turn with t, below rope.b2 with h, the
+    // rest with w.
+    constexpr int kPitch = 272;  // bytes per staged token row (256 + 16 keeps writes conflict-free)
+    lds_u8 *stg = lds + wave * 32 * kPitch;
+
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        const int m = t0 + wt * 128 + tb * 32 + col;  // token row (batch-major)
+        const int mt = t0 + wt * 128 + tb * 32;  // first token row of the block
+        const int m = mt + col;
+        float y[4][16];
         float ss = 0.f;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                float b4[4];
-                load4(bias ? bias + cw : nullptr, cb, r4, 0.f, b4);
+                const float b4[4] = {lo(bw[cb][r4][0]), hi(bw[cb][r4][0]), lo(bw[cb][r4][1]), hi(bw[cb][r4][1])};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float y = acc[cb][tb][4 * r4 + e] + b4[e];
-                    acc[cb][tb][4 * r4 + e] = y;
-                    ss = fmaf(y, y, ss);
+                    y[cb][4 * r4 + e] = acc[cb][tb][4 * r4 + e] + b4[e];
+                    ss = fmaf(y[cb][4 * r4 + e], y[cb][4 * r4 + e], ss);
                 }
             }
         if (gain) {
@@ -216,40 +225,56 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    float g4[4];
-                    load4(gain + hc, cb, r4, 1.f, g4);
+                    const float g4[4] = {lo(gw[cb][r4][0]), hi(gw[cb][r4][0]), lo(gw[cb][r4][1]),
+                                         hi(gw[cb][r4][1])};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[cb][tb][4 * r4 + e] *= sc * g4[e];
+                    for (int e = 0; e < 4; ++e) y[cb][4 * r4 + e] *= sc * g4[e];
                 }
         }
         if (rot) {
             const int n = m % g.N;
-            const float pos[3] = {(float)(n / HW), (float)((n / g.Wp) % g.Hp), (float)(n % g.Wp)};
+            const float pt = (float)(n / HW), ph = (float)((n / g.Wp) % g.Hp), pw = (float)(n % g.Wp);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int pr = (cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3)) >> 1;  // pair index
+                for (int rp = 0; rp < 8; ++rp) {
+                    const int p0 = cb * 16 + 4 * (rp >> 1) + (rp & 1);
+                    const int pr = p0 + 2 * half;
+                    const float pos = pr < rope.b1 ? pt : (pr < rope.b2 ? ph : pw);
+                    const float fq = half ? rope.freq_rev[p0 + 2] : rope.freq_rev[p0];
                     // Angle in revolutions, reduced to [0, 1) for v_sin/v_cos.
-                    const float rev = __builtin_amdgcn_fractf(pos[rope.axis[pr]] * rope.freq_rev[pr]);
+                    const float rev = __builtin_amdgcn_fractf(pos * fq);
                     const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
-                    const float re = acc[cb][tb][r], im = acc[cb][tb][r + 1];
-                    acc[cb][tb][r] = re * cs - im * sn;
-                    acc[cb][tb][r + 1] = re * sn + im * cs;
+                    const int r = 2 * rp;
+                    const float re = y[cb][r], im = y[cb][r + 1];
+                    y[cb][r] = re * cs - im * sn;
+                    y[cb][r + 1] = re * sn + im * cs;
                 }
         }
-        if (m < g.M) {
-            uint16_t *op = out + (int64_t)m * dim + hc;
+        // Stage: token col's row, channels cb*32 + 8*r4 + 4*half .. +3.
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    u32x2 st;
-                    st[0] = pack_bf16x2(acc[cb][tb][4 * r4 + 0], acc[cb][tb][4 * r4 + 1]);
-                    st[1] = pack_bf16x2(acc[cb][tb][4 * r4 + 2], acc[cb][tb][4 * r4 + 3]);
-                    *(u32x2 *)(op + cb * 32 + 8 * r4 + 4 * half) = st;
-                }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                u32x2 st;
+                st[0] = pack_bf16x2(y[cb][4 * r4 + 0], y[cb][4 * r4 + 1]);
+                st[1] = pack_bf16x2(y[cb][4 * r4 + 2], y[cb][4 * r4 + 3]);
+                *(__attribute__((address_space(3))) u32x2 *)(stg + col * kPitch + (cb * 32 + 8 * r4 + 4 * half) * 2) =
+                    st;
+            }
+        // The region is this wave's own: its LDS writes complete in order
+        // before the reads below.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        // Rows back out: 16 lanes per 256-byte row, 4 rows per read.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const u32x4 d = *(const __attribute__((address_space(3))) u32x4 *)(stg + row * kPitch + (lane & 15) * 16);
+            if (mt + row < g.M) *(u32x4 *)(out + (int64_t)(mt + row) * dim + hc + (lane & 15) * 8) = d;
         }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
     }
 #endif
 }

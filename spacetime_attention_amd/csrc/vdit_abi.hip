@@ -231,11 +231,11 @@ vdit_status_t vdit_qkv_proj(const void *x, const void *w, const void *bias, cons
     if (rope_on) {
         int j = 0;
         for (int a = 0; a < 3; ++a)
-            for (int jj = 0; jj < width[a] / 2; ++jj, ++j) {
-                rope.axis[j] = (unsigned char)a;
+            for (int jj = 0; jj < width[a] / 2; ++jj, ++j)
                 rope.freq_rev[j] = (float)(std::pow((double)theta, -2.0 * jj / (double)width[a]) /
                                            6.283185307179586476925286766559);
-            }
+        rope.b1 = d_t / 2;
+        rope.b2 = (d_t + d_h) / 2;
     }
     return launch_status(launch_qkv_proj_bf16(x, w, bias, gamma_q, gamma_k, q, k, v, g, rope, st));
 }

@@ -107,11 +107,12 @@ struct QkvGeom {
     int M, N, Hp, Wp, dim, D;
     float eps;
 };
-// Rotation for the bf16 kernel: per pair j (< 64) its axis and frequency in
-// revolutions per grid step (theta^(-2jj/d_a) / (2 pi)); on = 0 disables it.
+// Rotation for the bf16 kernel: per pair j (< 64) its frequency in
+// revolutions per grid step (theta^(-2jj/d_a) / (2 pi)); pairs j < b1 turn
+// with t, b1 <= j < b2 with h, the rest with w; on = 0 disables it.
 struct QkvRope {
     float freq_rev[64];
-    unsigned char axis[64];
+    int b1, b2;
     int on;
 };
 hipError_t launch_qkv_proj_bf16(const void *x, const void *w, const void *bias, const void *gq, const void *gk,
