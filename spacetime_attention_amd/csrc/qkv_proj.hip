@@ -37,6 +37,7 @@ constexpr int kTileC = 256;  // channels per workgroup
 constexpr int kTileT = 256;  // tokens per workgroup
 constexpr int kBK = 64;      // k per LDS stage
 constexpr int kThreads = 256;
+constexpr int kGroupT = 8;   // token tiles per ordering group
 constexpr int kRowBytes = kBK * 2;                  // 128 bytes of one tile row
 constexpr int kTileBytes = kTileC * kRowBytes;      // 32 KB (W or x tile)
 constexpr int kStageBytes = 2 * kTileBytes;         // W tile then x tile
@@ -72,7 +73,15 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     const int nct = (3 * dim + kTileC - 1) / kTileC;
     const int ntt = (g.M + kTileT - 1) / kTileT;
     const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)(nct * ntt));
-    const int ct = (int)(id % nct), tt = (int)(id / nct);
+    // Tiles are taken in groups of kGroupT token tiles: within a group the
+    // token tile varies fastest, then the channel tile, so the workgroups
+    // one XCD runs together (a contiguous run of ids) cover a few channel
+    // tiles of several token tiles and share both operands' rows in its L2.
+    const int grp = (int)(id / (uint32_t)(kGroupT * nct));
+    const int gt0 = grp * kGroupT;
+    const int gsz = min(kGroupT, ntt - gt0);
+    const int rem = (int)(id - (uint32_t)grp * kGroupT * nct);
+    const int ct = rem / gsz, tt = gt0 + rem % gsz;
     const int c0 = ct * kTileC, t0 = tt * kTileT;
 
     const int tid = threadIdx.x, lane = tid & 63;
