@@ -119,6 +119,139 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One 64-key tile whose K tile sits at LDS byte offset B0 (its V tile
+// follows at B0 + TILE): S^T for both 32-key blocks, the online softmax over
+// the tile, then O^T += V^T P^T. kvalid is the number of the tile's keys that
+// exist; after_s() runs once the S^T products are issued (the queries are no
+// longer needed after that point).
+template <int D, int QB, int NW, typename AfterS>
+__device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
+                                           const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[QB][D / 16],
+                                           f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
+                                           float c, int kvalid, int half, AfterS after_s)
+{
+    using S = FlashShape<D, QB, NW>;
+    constexpr int RB = D * 2;  // bytes per row
+    // LDS operand reads run one step ahead of the MFMAs that use them,
+    // in a second set of registers; scheduling fences keep the compiler
+    // from sinking them back to their uses.
+    bf16x8 ka[2][2];
+    auto rdk = [&](int ks, int slot) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+            ka[slot][kb2] = *(const __attribute__((address_space(3))) bf16x8 *)(
+                lds + kofs[ks] + (B0 + kb2 * 32 * RB));
+    };
+    bf16x4 va[2][S::DB][2];
+    auto rdv = [&](int st, int slot) {
+        const uint32_t off = B0 + S::TILE + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+            va[slot][db][0] = lds_read_tr(lds + (vofs[db] - S::TILE) + off);
+            va[slot][db][1] = lds_read_tr(lds + (vofs[db] - S::TILE) + (off + 8 * RB));
+        }
+    };
+
+    // S^T = K Q^T for both 32-key blocks.
+    f32x16 sacc[2][QB];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb] = (f32x16){};
+    rdk(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+        if (ks + 1 < S::KS) rdk(ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb2], qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
+    }
+    after_s();
+    // The first 16-key step's V operands load under the softmax.
+    rdv(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Keys past the end of the segment (last tile only).
+    if (kvalid < kBN) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (key >= kvalid)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb][r] = -INFINITY;
+            }
+    }
+
+    // Online softmax in the exp2 domain: x = s * scale * log2(e).
+    // Probabilities are first formed against the current reference
+    // maximum; only if a lane's tile sum leaves the budget (or is not
+    // finite, as on the first tile) does the wave take the row maximum,
+    // raise the reference, rescale and form them again.
+    bf16x8 pop[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        float ls = 0.f;
+        auto probs = [&]() {
+            const float nm = -mref[qb];
+            ls = 0.f;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
+                        ls += p[e];
+                    }
+                    u32x4 pk;
+                    pk[0] = pack_bf16x2(p[0], p[1]);
+                    pk[1] = pack_bf16x2(p[2], p[3]);
+                    pk[2] = pack_bf16x2(p[4], p[5]);
+                    pk[3] = pack_bf16x2(p[6], p[7]);
+                    pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
+                }
+        };
+        probs();
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
+            float mx = sacc[0][qb][0];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
+            mx = pair_max(mx) * c;
+            const float mnew = fmaxf(mx, mref[qb]);
+            const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
+            mref[qb] = mnew;
+            lsum[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
+            probs();
+        }
+        lsum[qb] += ls;
+    }
+
+    // O^T += V^T P^T over the tile's four 16-key steps.
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (st + 1 < 4) rdv(st + 1, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+            const bf16x8 a = __builtin_shufflevector(va[st & 1][db][0], va[st & 1][db][1], 0, 1, 2, 3, 4,
+                                                     5, 6, 7);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][st >> 1][st & 1], oacc[db][qb], 0, 0, 0);
+        }
+    }
+}
+
 // PASS (0 full, 1 spatial, 2 cross, 3 window) names the instantiation, so
 // that profiles attribute the passes separately; the first three run the
 // same code. L is the number of queries and Lk the number of keys per
@@ -311,130 +444,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
     const int ntiles = (Lk + kBN - 1) / kBN;
 
-    // One 64-key tile held in LDS buffer BUF: S^T for both 32-key blocks,
-    // the online softmax over the tile, then O^T += V^T P^T.
     auto tile = [&](auto bufc, int j) {
-        constexpr int BUF = decltype(bufc)::value;
-        constexpr uint32_t B0 = BUF * 2 * S::TILE;
-        constexpr int RB = D * 2;  // bytes per row
-        // LDS operand reads run one step ahead of the MFMAs that use them,
-        // in a second set of registers; scheduling fences keep the compiler
-        // from sinking them back to their uses.
-        bf16x8 ka[2][2];
-        auto rdk = [&](int ks, int slot) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-                ka[slot][kb2] = *(const __attribute__((address_space(3))) bf16x8 *)(
-                    lds + kofs[ks] + (B0 + kb2 * 32 * RB));
-        };
-        bf16x4 va[2][S::DB][2];
-        auto rdv = [&](int st, int slot) {
-            const uint32_t off = B0 + S::TILE + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
-#pragma unroll
-            for (int db = 0; db < S::DB; ++db) {
-                va[slot][db][0] = lds_read_tr(lds + (vofs[db] - S::TILE) + off);
-                va[slot][db][1] = lds_read_tr(lds + (vofs[db] - S::TILE) + (off + 8 * RB));
-            }
-        };
-
-        // S^T = K Q^T for both 32-key blocks.
-        f32x16 sacc[2][QB];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb] = (f32x16){};
-        rdk(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-            if (ks + 1 < S::KS) rdk(ks + 1, (ks + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb2], qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
-        }
-        // The first 16-key step's V operands load under the softmax.
-        rdv(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // Keys past the end of the segment (last tile only).
-        const int kvalid = Lk - j * kBN;
-        if (kvalid < kBN) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (key >= kvalid)
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb][r] = -INFINITY;
-                }
-        }
-
-        // Online softmax in the exp2 domain: x = s * scale * log2(e).
-        // Probabilities are first formed against the current reference
-        // maximum; only if a lane's tile sum leaves the budget (or is not
-        // finite, as on the first tile) does the wave take the row maximum,
-        // raise the reference, rescale and form them again.
-        bf16x8 pop[QB][2][2];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float ls = 0.f;
-            auto probs = [&]() {
-                const float nm = -mref[qb];
-                ls = 0.f;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        float p[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
-                            ls += p[e];
-                        }
-                        u32x4 pk;
-                        pk[0] = pack_bf16x2(p[0], p[1]);
-                        pk[1] = pack_bf16x2(p[2], p[3]);
-                        pk[2] = pack_bf16x2(p[4], p[5]);
-                        pk[3] = pack_bf16x2(p[6], p[7]);
-                        pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
-                    }
-            };
-            probs();
-            if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
-                float mx = sacc[0][qb][0];
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
-                mx = pair_max(mx) * c;
-                const float mnew = fmaxf(mx, mref[qb]);
-                const float alpha = __builtin_amdgcn_exp2f(mref[qb] - mnew);
-                mref[qb] = mnew;
-                lsum[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
-                probs();
-            }
-            lsum[qb] += ls;
-        }
-
-        // O^T += V^T P^T over the tile's four 16-key steps.
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            if (st + 1 < 4) rdv(st + 1, (st + 1) & 1);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < S::DB; ++db) {
-                const bf16x8 a = __builtin_shufflevector(va[st & 1][db][0], va[st & 1][db][1], 0, 1, 2, 3, 4,
-                                                         5, 6, 7);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][st >> 1][st & 1], oacc[db][qb], 0, 0, 0);
-            }
-        }
+        constexpr uint32_t B0 = decltype(bufc)::value * 2 * S::TILE;
+        flash_tile<D, QB, NW>(lds, B0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - j * kBN, half, [] {});
     };
 
     load_tile(0, 0);
