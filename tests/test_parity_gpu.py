@@ -15,7 +15,7 @@ import torch
 import oracle
 import spacetime_attention_amd as vd
 from synthetic_inputs import (CROSS_WORKLOADS, QKV_WORKLOADS, WORKLOADS, CrossWorkload, QkvWorkload, bf16_bits,
-                              bf16_to_f32, draw, sample_rows, small_grid)
+                              bf16_to_f32, draw, round_bf16, sample_rows, small_grid)
 from tests.parity_util import assert_close, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -452,3 +452,38 @@ def test_qkv_proj_480p_sampled():
     idx = torch.from_numpy(rows).cuda()
     for t, g, r in zip("qkv", got, ref):
         assert_close(to_host(g[:, idx]), r, "bf16", f"qkv_480p/{t}")
+
+
+def test_qkv_proj_14b_width():
+    # The 14B model's width (40 heads x 128, dim 5,120): 80 K stages and 60
+    # channel tiles, on a small grid whose token count leaves a ragged tile.
+    w = QkvWorkload("qkv_14b", 1, 5, 16, 20, 40, 128, "bf16", seed=31, rope_split=(44, 42, 42))
+    _announce("qkv_proj 14B width: [1,1600,5120] x [15360,5120]")
+    rows = sample_rows(w.N, 37, offset=5)
+    got, ref = _qkv_case(w, w.draw(), w.rope_split, True, True, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    for t, g, r in zip("qkv", got, ref):
+        assert_close(to_host(g[:, idx]), r, "bf16", f"qkv_14b/{t}")
+
+
+def test_attn1_input_chain():
+    # The self-attention input path of one block, end to end: patchify of a
+    # latent, projection to Q/K/V with per-head RMSNorm and RoPE on Q and K,
+    # then full 3D attention; the oracle chains its own routines in fp64.
+    grid, heads, D, C = (3, 6, 8), 2, 128, 16
+    dim = heads * D
+    _announce(f"attn1 chain: latent (1,{C},3,12,16) -> [1,144,{dim}] -> qkv -> full attention")
+    d = draw(51, [("x", (1, C, 3, 12, 16), 1.0), ("pw", (dim, C, 1, 2, 2), 0.02), ("w", (3 * dim, dim), 0.02),
+                  ("b", (3 * dim,), 0.02)], "bf16")
+    g = draw(52, [("gq", (dim,), 0.02), ("gk", (dim,), 0.02)], "f32")
+    gq, gk = (round_bf16(g[n].f32 + np.float32(1.0)) for n in ("gq", "gk"))
+    dev = {n: to_dev(d[n]) for n in d}
+    gq_d, gk_d = (torch.from_numpy(bf16_bits(t).view(np.int16)).view(torch.bfloat16).cuda() for t in (gq, gk))
+    tok = vd.patchify(dev["x"], dev["pw"], heads=heads, head_dim=D)
+    q, k, v = vd.qkv_proj(tok, dev["w"], dev["b"], gq_d, gk_d, grid=grid, heads=heads, head_dim=D,
+                          split=(44, 42, 42))
+    got = to_host(vd.attn_full(q, k, v, grid))
+    rtok = oracle.patchify(d["x"].f32, d["pw"].f32)
+    rq, rk, rv = oracle.qkv_proj(rtok, d["w"].f32, d["b"].f32, gq, gk, grid, heads, D, (44, 42, 42))
+    ref = oracle.attention(rq, rk, rv, grid, "full")
+    assert_close(got, ref, "bf16", "attn1_chain")
