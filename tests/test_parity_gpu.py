@@ -487,3 +487,17 @@ def test_attn1_input_chain():
     rq, rk, rv = oracle.qkv_proj(rtok, d["w"].f32, d["b"].f32, gq, gk, grid, heads, D, (44, 42, 42))
     ref = oracle.attention(rq, rk, rv, grid, "full")
     assert_close(got, ref, "bf16", "attn1_chain")
+
+
+@pytest.mark.parametrize("T", [24, 25, 32, 33, 64])
+def test_temporal_block_boundaries(T):
+    # The temporal kernel picks its layout by T: up to 24, up to 32, up to 64
+    # frames (two 32-key blocks); each side of every boundary, up to the
+    # 64-frame limit.
+    grid = (T, 3, 5)
+    _announce(f"temporal bf16 T={T} grid={grid}")
+    w = small_grid(f"t{T}", 2, *grid, 3, 128, "bf16", seed=400 + T)
+    d, (q, k, v) = _qkv(w)
+    got = to_host(vd.attn_temporal(q, k, v, grid))
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, "temporal")
+    assert_close(got, ref, "bf16", f"temporal/T{T}")
