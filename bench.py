@@ -46,6 +46,9 @@ def _parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (profiling runs)")
+    p.add_argument("--with-720p", action="store_true",
+                   help="also time full attention at 720p [1,75600,40,128] after the step (same kernel as "
+                        "the 480p full pass, so it stays out of the default run that profiles summarise)")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one plain 1 GiB device copy first (HBM counter calibration)")
     return p.parse_args()
@@ -221,6 +224,8 @@ def main():
 
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch)}
+    if args.with_720p:
+        result["full_720p"] = bench_full_720p(vd, torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
         result["cpu_baseline"]["gpu_over_cpu"] = per_pass["full"]["tflops"] / result["cpu_baseline"]["value"]
@@ -248,6 +253,36 @@ def bench_cross(vd, torch, iters: int = 20):
     flop = 4.0 * w.B * w.heads * w.Nq * w.Nk * w.head_dim
     return {"workload": f"q [{w.B},{w.Nq},{w.heads},{w.head_dim}] x k/v [{w.B},{w.Nk},{w.heads},{w.head_dim}]",
             "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+
+def bench_full_720p(vd, torch, iters: int = 5):
+    """Full attention at the 14B-shaped 720p size, timed on its own after the
+    step: [1,75600,40,128] bf16 Q/K/V drawn N(0,1) on the device from a fixed
+    seed (the sampled parity test covers the same shape with the host draw)."""
+    from synthetic_inputs import WORKLOADS
+    w = WORKLOADS["720p_full"]
+    grid = (w.T, w.Hp, w.Wp)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    shape = (w.B, w.N, w.heads, w.head_dim)
+    q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    for _ in range(2):
+        vd.attn_full(q, k, v, grid, out=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        vd.attn_full(q, k, v, grid, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    flop = 4.0 * w.B * w.heads * float(w.N) ** 2 * w.head_dim
+    del q, k, v, o
+    return {"workload": f"[{w.B},{w.N},{w.heads},{w.head_dim}] grid {grid}", "ms": ms,
+            "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS,
+            "tokens_per_s": w.B * w.N / (ms * 1e-3)}
 
 
 def window_flop(w, window) -> float:

@@ -15,7 +15,7 @@
 // mixed-radix decomposition of j over the box's clipped extents, and key
 // rows are advanced by that radix from one 64-key tile to the next.
 //
-// Layout of the work (one workgroup = 4 wavefronts = BM query tokens):
+// Layout of the work (one workgroup = 4 or 8 wavefronts of 32 queries):
 //  * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //    the A operand is a 32-key block of K read from LDS, the B operand the
 //    wave's queries kept in registers for the whole pass. In the result each
@@ -28,7 +28,7 @@
 //    registers already hold a valid B operand (no shuffles). V^T comes from
 //    a row-major V tile in LDS through ds_read_b64_tr_b16, which hands each
 //    lane four consecutive keys of one feature column.
-//  * K and V tiles of 64 keys are double-buffered in LDS and filled by
+//  * K and V tiles of 64 keys are buffered in LDS and filled by
 //    buffer loads that write LDS directly (no staging registers): lane l of a
 //    load lands at byte 16*l of the wave's 1 KB destination, so each lane
 //    fetches the global chunk that belongs at that swizzled LDS slot. The
@@ -37,6 +37,12 @@
 //    issued before the current tile's products. Chunk-XOR swizzles keep the
 //    K reads (32 rows, one 16-byte chunk each) and the transposed V reads
 //    (8 rows x 64 bytes) free of bank conflicts.
+//  * Full attention (8 wavefronts, two per SIMD: waves w and w+4 share one)
+//    runs a ping-pong schedule: each wave alternates an all-MFMA phase
+//    (V^T P^T of the previous tile, then S^T of the current one) with an
+//    all-VALU phase (the current tile's softmax), with a workgroup barrier
+//    after every phase, and waves 4..7 run one phase behind waves 0..3, so
+//    one wave's exponentials always run under the other's matrix products.
 //  * The reference maximum of the online softmax is raised lazily: a tile's
 //    probabilities are formed against the current reference, and only when
 //    a lane's tile sum exceeds 2^32 (or is not finite, as on the first tile)
@@ -105,6 +111,14 @@ constexpr int kBufferFlags = 0x00020000;
 // ones that write LDS directly) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier that orders LDS accesses only: vector-memory loads that
+// are still in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const lds_u8 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p);
 }
@@ -119,18 +133,16 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-key tile whose K tile sits at LDS byte offset B0 (its V tile
-// follows at B0 + TILE): S^T for both 32-key blocks, the online softmax over
-// the tile, then O^T += V^T P^T. kvalid is the number of the tile's keys that
-// exist; after_s() runs once the S^T products are issued (the queries are no
-// longer needed after that point).
-template <int D, int QB, int NW, typename AfterS>
-__device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
-                                           const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[QB][D / 16],
-                                           f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
-                                           float c, int kvalid, int half, AfterS after_s)
+// The three parts of one 64-key tile. flash_s forms S^T = K Q^T for both
+// 32-key blocks from the K tile at LDS byte offset KB0; flash_softmax takes
+// the online softmax over those scores (kvalid = number of the tile's keys
+// that exist) and leaves the probabilities P^T as bf16 MFMA operands;
+// flash_pv adds V^T P^T to O^T from the V tile at LDS byte offset VB0.
+template <int D, int QB>
+__device__ __forceinline__ void flash_s(const lds_u8 *lds, uint32_t KB0, const uint32_t (&kofs)[D / 16],
+                                        const bf16x8 (&qop)[QB][D / 16], f32x16 (&sacc)[2][QB])
 {
-    using S = FlashShape<D, QB, NW>;
+    constexpr int KS = D / 16;
     constexpr int RB = D * 2;  // bytes per row
     // LDS operand reads run one step ahead of the MFMAs that use them,
     // in a second set of registers; scheduling fences keep the compiler
@@ -140,28 +152,16 @@ __device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
             ka[slot][kb2] = *(const __attribute__((address_space(3))) bf16x8 *)(
-                lds + kofs[ks] + (B0 + kb2 * 32 * RB));
+                lds + kofs[ks] + (KB0 + kb2 * 32 * RB));
     };
-    bf16x4 va[2][S::DB][2];
-    auto rdv = [&](int st, int slot) {
-        const uint32_t off = B0 + S::TILE + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-            va[slot][db][0] = lds_read_tr(lds + (vofs[db] - S::TILE) + off);
-            va[slot][db][1] = lds_read_tr(lds + (vofs[db] - S::TILE) + (off + 8 * RB));
-        }
-    };
-
-    // S^T = K Q^T for both 32-key blocks.
-    f32x16 sacc[2][QB];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[kb2][qb] = (f32x16){};
     rdk(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-        if (ks + 1 < S::KS) rdk(ks + 1, (ks + 1) & 1);
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) rdk(ks + 1, (ks + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -169,11 +169,14 @@ __device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const
             for (int qb = 0; qb < QB; ++qb)
                 sacc[kb2][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1][kb2], qop[qb][ks], sacc[kb2][qb], 0, 0, 0);
     }
-    after_s();
-    // The first 16-key step's V operands load under the softmax.
-    rdv(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+}
 
+template <int D, int QB>
+__device__ __forceinline__ void flash_softmax(f32x16 (&sacc)[2][QB], bf16x8 (&pop)[QB][2][2],
+                                              f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
+                                              float c, int kvalid, int half)
+{
+    constexpr int DB = D / 32;
     // Keys past the end of the segment (last tile only).
     if (kvalid < kBN) {
 #pragma unroll
@@ -192,30 +195,41 @@ __device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const
     // maximum; only if a lane's tile sum leaves the budget (or is not
     // finite, as on the first tile) does the wave take the row maximum,
     // raise the reference, rescale and form them again.
-    bf16x8 pop[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         float ls = 0.f;
+        // A 32-key block at a time: its 16 exponents, then the 16
+        // exponentials, then a pairwise sum and the bf16 packing, each group
+        // fenced so that the wave issues independent instructions back to
+        // back instead of waiting on each result in turn.
         auto probs = [&]() {
             const float nm = -mref[qb];
             ls = 0.f;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                float p[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = fmaf(sacc[kb2][qb][r], c, nm);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(p[r]);
+                __builtin_amdgcn_sched_barrier(0);
+                float t[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) t[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+                ls += (t[0] + t[1]) + (t[2] + t[3]);
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    float p[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][qb][8 * s2 + e], c, nm));
-                        ls += p[e];
-                    }
                     u32x4 pk;
-                    pk[0] = pack_bf16x2(p[0], p[1]);
-                    pk[1] = pack_bf16x2(p[2], p[3]);
-                    pk[2] = pack_bf16x2(p[4], p[5]);
-                    pk[3] = pack_bf16x2(p[6], p[7]);
+                    pk[0] = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+                    pk[1] = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+                    pk[2] = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+                    pk[3] = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
                     pop[qb][kb2][s2] = __builtin_bit_cast(bf16x8, pk);
                 }
+            }
         };
         probs();
         if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
@@ -230,19 +244,37 @@ __device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const
             mref[qb] = mnew;
             lsum[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < S::DB; ++db) oacc[db][qb] *= alpha;
+            for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
             probs();
         }
         lsum[qb] += ls;
     }
+}
 
+template <int D, int QB>
+__device__ __forceinline__ void flash_pv(const lds_u8 *lds, uint32_t VB0, const uint32_t (&vofs)[D / 32],
+                                         const bf16x8 (&pop)[QB][2][2], f32x16 (&oacc)[D / 32][QB])
+{
+    constexpr int DB = D / 32;
+    constexpr int RB = D * 2;  // bytes per row
+    constexpr int TILE = kBN * RB;
+    bf16x4 va[2][DB][2];
+    auto rdv = [&](int st, int slot) {
+        const uint32_t off = VB0 + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            va[slot][db][0] = lds_read_tr(lds + (vofs[db] - TILE) + off);
+            va[slot][db][1] = lds_read_tr(lds + (vofs[db] - TILE) + (off + 8 * RB));
+        }
+    };
+    rdv(0, 0);
     // O^T += V^T P^T over the tile's four 16-key steps.
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         if (st + 1 < 4) rdv(st + 1, (st + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
+        for (int db = 0; db < DB; ++db) {
             const bf16x8 a = __builtin_shufflevector(va[st & 1][db][0], va[st & 1][db][1], 0, 1, 2, 3, 4,
                                                      5, 6, 7);
 #pragma unroll
@@ -250,6 +282,22 @@ __device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const
                 oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pop[qb][st >> 1][st & 1], oacc[db][qb], 0, 0, 0);
         }
     }
+}
+
+// One whole 64-key tile whose K tile sits at LDS byte offset B0 and its V
+// tile at B0 + TILE. after_s() runs once the S^T products are issued.
+template <int D, int QB, typename AfterS>
+__device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
+                                           const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[QB][D / 16],
+                                           f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
+                                           float c, int kvalid, int half, AfterS after_s)
+{
+    f32x16 sacc[2][QB];
+    bf16x8 pop[QB][2][2];
+    flash_s<D, QB>(lds, B0, kofs, qop, sacc);
+    after_s();
+    flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, kvalid, half);
+    flash_pv<D, QB>(lds, B0 + kBN * D * 2, vofs, pop, oacc);
 }
 
 // PASS (0 full, 1 spatial, 2 cross, 3 window) names the instantiation, so
@@ -266,7 +314,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using S = FlashShape<D, QB, NW>;
     constexpr bool WIN = PASS == 3;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * S::TILE];
+    // The full pass (8 waves) runs two 4-wave groups out of phase over three
+    // K and three V buffers; the other passes alternate two K/V pairs.
+    constexpr bool PP = NW == 8 && !WIN;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[(PP ? 6 : 4) * S::TILE];
     lds_u8 *lds = (lds_u8 *)smem;
 
     const int nqb = WIN ? wg.nqb : (L + S::BM - 1) / S::BM;
@@ -408,6 +459,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         }
     };
 
+    // K or V alone (full pass): tile at key t0 into LDS byte offset dst.
+    auto load_one = [&](__amdgpu_buffer_rsrc_t rs_, const uint32_t (&off)[S::LOADS], int t0, uint32_t dst) {
+        const uint32_t so = (uint32_t)((int64_t)t0 * rs * 2);
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_, (lds_void *)(lds + dst + (wave * S::LOADS + i) * 1024), 16,
+                                                     off[i], so, 0, 0);
+    };
+
     // Per-lane LDS byte offsets of the operand reads, for buffer 0 and key
     // block 0. Every other read adds a compile-time constant (buffer, key
     // block, 16-key step, upper 8 rows), which the ds_read offset field holds:
@@ -446,9 +506,55 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
     auto tile = [&](auto bufc, int j) {
         constexpr uint32_t B0 = decltype(bufc)::value * 2 * S::TILE;
-        flash_tile<D, QB, NW>(lds, B0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - j * kBN, half, [] {});
+        flash_tile<D, QB>(lds, B0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - j * kBN, half, [] {});
     };
 
+    if constexpr (PP) {
+        // Each wave alternates an MFMA phase X(j) = [O^T += V^T P^T for tile
+        // j-1, then S^T for tile j] with a VALU phase Y(j) = the softmax of
+        // tile j, and a barrier ends every phase. Waves 4..7 start one
+        // barrier late, so while waves 0..3 run X they run Y and the other
+        // way round: each SIMD holds one wave of each group, so one wave's
+        // softmax runs under the other's MFMAs. K(j) is read in X(j) and V(j)
+        // in X(j+1); each sits in buffer j % 3 of its kind. Y(j) loads K(j+2)
+        // and V(j+1), whose buffers (those of K(j-1) and V(j-2)) both groups
+        // left at the latest in X(j-1), and each wave waits for its share
+        // before the barrier that ends Y(j), ahead of their first reader.
+        const bool late = wave >= 4;
+        constexpr uint32_t VB = 3 * S::TILE;  // V buffers follow the K buffers
+        f32x16 sacc[2][QB];
+        bf16x8 pop[QB][2][2];
+        load_one(krs, koff, 0, 0);
+        if (ntiles > 1) load_one(krs, koff, kBN, S::TILE);
+        load_one(vrs, voff, 0, VB);
+        wait_vmem();
+        __syncthreads();
+        if (late) lds_barrier();
+        auto phase = [&](auto bufc, int j) {
+            constexpr uint32_t b = decltype(bufc)::value;
+            constexpr uint32_t bp = (b + 2) % 3, b1 = (b + 1) % 3, b2 = (b + 2) % 3;
+            // X(j)
+            if (busy) {
+                if (j > 0) flash_pv<D, QB>(lds, VB + bp * S::TILE, vofs, pop, oacc);
+                if (j < ntiles) flash_s<D, QB>(lds, b * S::TILE, kofs, qop, sacc);
+            }
+            lds_barrier();
+            if (j >= ntiles) return false;
+            // Y(j)
+            if (j + 2 < ntiles) load_one(krs, koff, (j + 2) * kBN, b2 * S::TILE);
+            if (j + 1 < ntiles) load_one(vrs, voff, (j + 1) * kBN, VB + b1 * S::TILE);
+            if (busy) flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, Lk - j * kBN, half);
+            wait_vmem();
+            lds_barrier();
+            return true;
+        };
+        for (int j = 0;; j += 3) {
+            if (!phase(std::integral_constant<uint32_t, 0>{}, j)) break;
+            if (!phase(std::integral_constant<uint32_t, 1>{}, j + 1)) break;
+            if (!phase(std::integral_constant<uint32_t, 2>{}, j + 2)) break;
+        }
+        if (!late) lds_barrier();
+    } else {
     load_tile(0, 0);
     wait_vmem();
     __syncthreads();
@@ -466,6 +572,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         if (busy) tile(std::integral_constant<int, 1>{}, j + 1);
         wait_vmem();
         __syncthreads();
+    }
     }
 
     // Normalise and store: lane holds query column `col`, features
