@@ -13,11 +13,12 @@
 // bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation): a workgroup owns
 // kTok tokens; it gathers their [kTok][K] patch matrix into LDS once and
 // sweeps all output channels in chunks of 128, each wave computing a
-// 32-channel x kTok-token block of C^T = W A^T with W read straight from
-// global (it is small and stays in L2). Each chunk is staged through LDS and
-// written as whole 256-byte row runs: at K = 64 the kernel writes 24x more
-// bytes than it reads, so coalesced stores set its speed. LDS is sized to the
-// actual patch length so several workgroups share a CU.
+// 32-channel x kTok-token block of C^T = W A^T with W and the bias read
+// straight from global (they are small and stay in L2), one chunk ahead.
+// Each chunk is staged through LDS (two alternating buffers, one barrier per
+// chunk) and written as whole 256-byte row runs: at K = 64 the kernel writes
+// 24x more bytes than it reads, so coalesced stores set its speed. LDS is
+// sized to the actual patch length so several workgroups share a CU.
 //
 // fp32 path: one thread per output element, a plain dot product (for the
 // small fp32 workloads that must agree with fp64 to 1e-5).
@@ -44,14 +45,15 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
                                                             uint16_t *__restrict__ tok, PatchGeom g, int K,
                                                             int Kp)
 {
-    // Dynamic LDS, sized to the patch length: the output chunk
-    // [kTok][kOut + 8] bf16, then the A tile [kTok][Kp + 8] bf16 (the 16-byte
-    // pads stagger rows over banks).
+    // Dynamic LDS, sized to the patch length: two output chunks
+    // [kTok][kOut + 8] bf16 (alternate chunks use alternate buffers), then
+    // the A tile [kTok][Kp + 8] bf16 (the 16-byte pads stagger rows over
+    // banks).
     extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
     const int arow = (Kp + 8) * 2;     // bytes per A row
     const int orow = (kOut + 8) * 2;   // bytes per output-chunk row
-    lds_u8 *ol = (lds_u8 *)dyn_lds;
-    lds_u8 *al = ol + kTok * orow;
+    lds_u8 *ol0 = (lds_u8 *)dyn_lds;
+    lds_u8 *al = ol0 + 2 * kTok * orow;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -124,15 +126,33 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
         }
         return v8;
     };
+    // Bias of chunk oc for this lane's rows: channels oc + wave*32 + 8*r4 +
+    // 4*half .. +4, one 8-byte load each (Dout is a multiple of 8 and bias is
+    // 16-byte aligned, so a run of 4 never straddles the end).
+    auto b_op = [&](int oc, int r4) {
+        const int ch = oc + wave * 32 + 8 * r4 + 4 * half;
+        u32x2 v = (u32x2){0u, 0u};
+        if (bias && ch < g.Dout) v = *(const u32x2 *)(bias + ch);
+        return v;
+    };
     constexpr int NS = KSC > 0 ? KSC : 1;
     bf16x8 wcur[NS], wnext[NS];
-    if constexpr (KSC > 0) {
-        if (c0 < c1)
+    u32x2 bcur[4], bnext[4];
+    if (c0 < c1) {
+        if constexpr (KSC > 0) {
 #pragma unroll
             for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = w_op(c0 * kOut, s2);
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = b_op(c0 * kOut, r4);
     }
     for (int ci = c0; ci < c1; ++ci) {
         const int oc = ci * kOut;
+        lds_u8 *ol = ol0 + ((ci - c0) & 1) * kTok * orow;
+        // The next chunk's bias loads are in flight during this chunk.
+        if (ci + 1 < c1)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) bnext[r4] = b_op(oc + kOut, r4);
         f32x16 acc[kTB];
 #pragma unroll
         for (int tb = 0; tb < kTB; ++tb) acc[tb] = (f32x16){};
@@ -166,8 +186,8 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
                 float vals[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float bv = 0.f;
-                    if (bias && oc + oo + e < g.Dout) bv = bf16_bits_to_f32(bias[oc + oo + e]);
+                    const uint32_t bw = bcur[r4][e >> 1];
+                    const float bv = __uint_as_float((e & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
                     vals[e] = acc[tb][4 * r4 + e] + bv;
                 }
                 u32x2 pk;
@@ -175,7 +195,15 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
                 pk[1] = pack_bf16x2(vals[2], vals[3]);
                 *(__attribute__((address_space(3))) u32x2 *)(ol + (tb * 32 + col) * orow + oo * 2) = pk;
             }
-        __syncthreads();
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = bnext[r4];
+        // One barrier per chunk: it orders this chunk's LDS writes before the
+        // reads below, and the previous chunk's reads of the other buffer
+        // before the next chunk's writes to it. It orders LDS only, so the
+        // global stores stay in flight across it.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         for (int idx = tid; idx < kTok * (kOut / 8); idx += 256) {
             const int r = idx / (kOut / 8), ch = idx % (kOut / 8);
             const int64_t m = m0 + r;
@@ -184,7 +212,6 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
                 *(u32x4 *)(tok + m * g.Dout + o0) = *(const __attribute__((address_space(3))) u32x4 *)(
                     ol + r * orow + ch * 16);
         }
-        __syncthreads();  // the output chunk is reused by the next chunk
     }
 }
 
@@ -222,7 +249,7 @@ hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, 
     if (Kp > kMaxK || g.Dout % 8) return hipErrorInvalidValue;
     const int64_t M = (int64_t)g.B * g.T * g.Hp * g.Wp;
     const dim3 grid((uint32_t)((M + kTok - 1) / kTok), kChunkSplit);
-    const size_t lds = (size_t)kTok * ((kOut + 8) + (Kp + 8)) * 2;
+    const size_t lds = (size_t)kTok * (2 * (kOut + 8) + (Kp + 8)) * 2;
     auto go = [&](auto kernel) {
         if (lds > 65536) {  // above the default dynamic-LDS limit (up to 50 KB at Kp = 512)
             const hipError_t e =

@@ -197,6 +197,20 @@ def test_patchify_small(dtype):
     assert_close(got, ref, dtype, f"patchify/{dtype}")
 
 
+@pytest.mark.parametrize("C,dout", [(16, 384), (12, 640), (16, 1536)])
+def test_patchify_bias_chunks(C, dout):
+    # Several 128-channel chunks with a bias (each chunk's bias is fetched
+    # one chunk ahead), a 1x2x2 brick, and a token count that leaves the last
+    # 32-token block ragged (3 x 7 x 5 = 105 tokens).
+    _announce(f"patchify bias chunks C={C} dout={dout}")
+    d = draw(43, [("x", (1, C, 3, 14, 10), 1.0), ("w", (dout, C, 1, 2, 2), 0.02), ("b", (dout,), 0.1)], "bf16")
+    x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
+    got = to_host(vd.patchify(x, wt, b, heads=dout // 128, head_dim=128))
+    ref = oracle.patchify(d["x"].f32, d["w"].f32, d["b"].f32)
+    assert got.shape == ref.shape == (1, 105, dout)
+    assert_close(got, ref, "bf16", f"patchify/C{C}/dout{dout}")
+
+
 # ----------------------------------------------------------------------------
 # Full-size workloads, sampled
 # ----------------------------------------------------------------------------
