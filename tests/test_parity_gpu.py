@@ -44,6 +44,12 @@ SMALL = [
     ("single_frame", 1, (1, 9, 15), 2, 128),
     ("long_time_40", 1, (40, 2, 3), 2, 128),
     ("one_token_frames", 2, (7, 1, 1), 2, 128),
+    # 100 tokens: only the first four 32-query wavefronts of an 8-wave
+    # workgroup have queries, so one group of the full pass's two phase
+    # groups runs alone; 2 key tiles.
+    ("first_group_only_100", 1, (4, 5, 5), 2, 128),
+    # 620 tokens: three query blocks (256, 256, 108), 10 key tiles.
+    ("three_blocks_620", 2, (5, 4, 31), 2, 128),
 ]
 
 
