@@ -27,7 +27,7 @@
 namespace vdit {
 namespace {
 
-constexpr int kTok = 32;   // tokens per workgroup
+constexpr int kTok = 64;   // tokens per workgroup
 constexpr int kTB = kTok / 32;  // 32-token MFMA blocks per workgroup
 constexpr int kChunkSplit = 1;  // workgroups that share one token block's channel chunks
 constexpr int kOut = 128;  // output channels per chunk
@@ -251,7 +251,7 @@ hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, 
     const dim3 grid((uint32_t)((M + kTok - 1) / kTok), kChunkSplit);
     const size_t lds = (size_t)kTok * (2 * (kOut + 8) + (Kp + 8)) * 2;
     auto go = [&](auto kernel) {
-        if (lds > 65536) {  // above the default dynamic-LDS limit (up to 50 KB at Kp = 512)
+        if (lds > 65536) {  // above the default dynamic-LDS limit (up to 99 KB at Kp = 512)
             const hipError_t e =
                 hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
