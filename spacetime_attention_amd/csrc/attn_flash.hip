@@ -514,8 +514,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         // j-1, then S^T for tile j] with a VALU phase Y(j) = the softmax of
         // tile j, and a barrier ends every phase. Waves 4..7 start one
         // barrier late, so while waves 0..3 run X they run Y and the other
-        // way round: each SIMD holds one wave of each group, so one wave's
-        // softmax runs under the other's MFMAs. K(j) is read in X(j) and V(j)
+        // way round: each SIMD holds one wave of each group (waves w and w+4
+        // share a SIMD), so one wave's softmax runs under the other's MFMAs.
+        // That placement only decides the overlap; the barrier protocol below
+        // is correct for any placement. K(j) is read in X(j) and V(j)
         // in X(j+1); each sits in buffer j % 3 of its kind. Y(j) loads K(j+2)
         // and V(j+1), whose buffers (those of K(j-1) and V(j-2)) both groups
         // left at the latest in X(j-1), and each wave waits for its share
