@@ -578,13 +578,17 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     }
 
     // Normalise and store: lane holds query column `col`, features
-    // db*32 + 8*(r/4) + 4*half + r%4.
+    // db*32 + 8*(r/4) + 4*half + r%4. The 32 rows are staged through this
+    // wave's own stretch of the (now idle) K/V buffers and written as whole
+    // rows, 16 bytes per lane, so every store instruction covers four
+    // contiguous rows instead of 16-byte pieces of 32.
+    {
+        constexpr int OP = D * 2 + 16;  // staging pitch (bytes): rows 16 bytes apart in the banks
+        static_assert(NW * 32 * OP <= (PP ? 6 : 4) * S::TILE, "staging fits the K/V buffers");
+        lds_u8 *st = lds + wave * 32 * OP;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float inv = 1.0f / pair_sum(lsum[qb]);
-        const int qi = q0 + qb * 32 + col;
-        if (qi < L) {
-            const int64_t orow = (int64_t)tok(qi) * rs;
+        for (int qb = 0; qb < QB; ++qb) {
+            const float inv = 1.0f / pair_sum(lsum[qb]);
 #pragma unroll
             for (int db = 0; db < S::DB; ++db)
 #pragma unroll
@@ -593,8 +597,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
                     u32x2 w;
                     w[0] = pack_bf16x2(oacc[db][qb][4 * r4 + 0] * inv, oacc[db][qb][4 * r4 + 1] * inv);
                     w[1] = pack_bf16x2(oacc[db][qb][4 * r4 + 2] * inv, oacc[db][qb][4 * r4 + 3] * inv);
-                    *(u32x2 *)(op + orow + d) = w;
+                    *(__attribute__((address_space(3))) u32x2 *)(st + col * OP + d * 2) = w;
                 }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's rows are in LDS
+            __builtin_amdgcn_wave_barrier();
+            constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+#pragma unroll
+            for (int i = 0; i < 32 * CPR / 64; ++i) {
+                const int idx = lane + 64 * i;
+                const int r = idx / CPR, ch = idx % CPR;
+                const int qi = q0 + qb * 32 + r;
+                const u32x4 val = *(const __attribute__((address_space(3))) u32x4 *)(st + r * OP + ch * 16);
+                if (qi < L) *(u32x4 *)(op + (int64_t)tok(qi) * rs + ch * 8) = val;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_wave_barrier();
         }
     }
 #endif
