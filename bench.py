@@ -49,6 +49,8 @@ def _parse():
     p.add_argument("--with-720p", action="store_true",
                    help="also time full attention at 720p [1,75600,40,128] after the step (same kernel as "
                         "the 480p full pass, so it stays out of the default run that profiles summarise)")
+    p.add_argument("--no-mfma-probe", action="store_true",
+                   help="skip the matrix-core rate probe that runs after the timed steps")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one plain 1 GiB device copy first (HBM counter calibration)")
     return p.parse_args()
@@ -226,10 +228,24 @@ def main():
                            "qkv_proj": bench_qkv(vd, torch)}
     if args.with_720p:
         result["full_720p"] = bench_full_720p(vd, torch)
+    if not args.no_mfma_probe:
+        result["mfma_ceiling"] = mfma_ceiling(achieved)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
         result["cpu_baseline"]["gpu_over_cpu"] = per_pass["full"]["tflops"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
+
+
+def mfma_ceiling(achieved_full: float):
+    """The bf16 MFMA rate this device sustains from registers alone (no
+    memory, no softmax), with near-constant and with random full-mantissa
+    operands, measured after the timed steps; and the full pass's rate as a
+    fraction of the random-operand figure."""
+    from spacetime_attention_amd import probe
+    out = {"kernel": "8 chains of v_mfma_f32_32x32x16_bf16 per wave, registers only (libvdit_probe.so)",
+           "near_constant": probe.mfma_rate(False), "random": probe.mfma_rate(True)}
+    out["full_over_random"] = achieved_full / out["random"]["tflops"]
+    return out
 
 
 def bench_cross(vd, torch, iters: int = 20):

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvdit.so")
+PROBE_LIB = os.path.join(HERE, "libvdit_probe.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["attn_flash.hip", "attn_temporal.hip", "attn_f32.hip", "patchify.hip", "rope3d.hip", "qkv_proj.hip",
@@ -52,8 +53,16 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # The matrix-core rate probe is a library of its own: nothing in the
+    # attention path links or loads it.
+    pobj = _compile("mfma_probe.hip")
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_LIB + ".tmp", pobj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -155,3 +155,24 @@ def test_qkv_proj_argument_errors(lib):
     assert call(q=Q + 16) == 6                       # output overlaps x
     assert call(k=O + 64) == 6                       # outputs overlap each other
     assert call(dt=3) == 7
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libvdit_probe.so exports what include/vdit_probe.h declares; bad
+    arguments return before anything is enqueued (fake pointer, no launch)."""
+    from spacetime_attention_amd import probe
+    if not os.path.exists(probe.PROBE_LIB_PATH):
+        from spacetime_attention_amd import build
+        build.build()
+    src = open(os.path.join(ROOT, "include", "vdit_probe.h")).read()
+    declared = sorted(set(re.findall(r"\b(vdit_[a-z0-9_]+)\s*\(", src)))
+    assert declared == sorted(probe.PROBE_EXPORTS)
+    plib = probe.load_probe_library()
+    for name in declared:
+        assert hasattr(plib, name), name
+    f = plib.vdit_probe_mfma_bf16
+    assert f(1, 100, 16, None, None) == 1          # NULL ticks
+    assert f(1, 0, 16, P, None) == 2               # iters < 1
+    assert f(1, 1 << 25, 16, P, None) == 2         # iters > 2^24
+    assert f(0, 100, 0, P, None) == 2              # nblocks < 1
+    assert f(0, 100, 1 << 17, P, None) == 2        # nblocks > 65536
