@@ -373,16 +373,21 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // every barrier, but skips the products and the softmax.
     const bool busy = q0 < L;
     bf16x8 qop[QB][S::KS];
+    // The 4-wave passes stage the queries through LDS (below); the full pass
+    // reads them straight into registers, once for its whole key loop.
+    constexpr bool QSTAGE = !PP && QB == 1 && NW == 4;
+    if constexpr (!QSTAGE) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qi = q0 + qb * 32 + col;
-        const int64_t qrow = (int64_t)tok(qi < L ? qi : 0) * rs;
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qi = q0 + qb * 32 + col;
+            const int64_t qrow = (int64_t)tok(qi < L ? qi : 0) * rs;
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-            if (qi < L)
-                qop[qb][ks] = *(const bf16x8 *)(qp + qrow + 16 * ks + 8 * half);
-            else
-                qop[qb][ks] = (bf16x8){};
+            for (int ks = 0; ks < S::KS; ++ks) {
+                if (qi < L)
+                    qop[qb][ks] = *(const bf16x8 *)(qp + qrow + 16 * ks + 8 * half);
+                else
+                    qop[qb][ks] = (bf16x8){};
+            }
         }
     }
 
@@ -557,9 +562,36 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         }
         if (!late) lds_barrier();
     } else {
+    if constexpr (QSTAGE) {
+        // The wave's 32 query rows go through LDS-direct loads (whole rows,
+        // four per instruction) into exactly the bytes its own loads of tile
+        // 1 fill later: rows 0-15 where its share of that K tile goes, rows
+        // 16-31 where its share of that V tile goes, chunk-swizzled like a K
+        // tile. Rows past the segment read as zeros.
+        static_assert(RPL * S::LOADS == 16, "a wave's share of one K or V tile is 16 rows");
+        const int nrecq = (int)(((int64_t)tok(L - 1) * rs + D) * 2);
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)qp, 0, nrecq, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < 2 * S::LOADS; ++i) {
+            const int r = RPL * i + lane / S::CH, qi = q0 + r;
+            const uint32_t off = qi < L ? (uint32_t)((int64_t)tok(qi) * rs * 2) +
+                                              (uint32_t)(((lane % S::CH) ^ swz_k<D>(r, 0)) * 16)
+                                        : 0x80000000u;
+            const uint32_t dst = (i < S::LOADS ? 2 : 3) * S::TILE + (wave * S::LOADS + i % S::LOADS) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(lds + dst), 16, off, 0, 0, 0);
+        }
+    }
     load_tile(0, 0);
     wait_vmem();
     __syncthreads();
+    if constexpr (QSTAGE) {
+        const uint32_t qb0 = (col < 16 ? 2 * S::TILE : 3 * S::TILE - 16 * D * 2) + wave * S::LOADS * 1024;
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks)
+            qop[0][ks] = *(const __attribute__((address_space(3))) bf16x8 *)(lds + qb0 + kofs[ks]);
+        // The first tile-1 load below overwrites these bytes.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     // Tiles alternate between the two LDS buffers; the loop body takes one
     // tile from each so that the buffer is a compile-time constant. The
     // other buffer was released by the barrier that ended the previous tile,
