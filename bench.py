@@ -236,6 +236,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _warm(torch, fn, min_ms: float = 100.0, at_least: int = 3):
+    """Launch fn until at least min_ms of device time has passed (and at least
+    `at_least` times). The passes timed on their own after the step follow
+    host-side input generation, during which the device idles and its clock
+    drops; the clock takes a few tens of milliseconds of load to come back."""
+    import time
+    t0 = time.perf_counter()
+    n = 0
+    while n < at_least or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def mfma_ceiling(achieved_full: float):
     """The bf16 MFMA rate this device sustains from registers alone (no
     memory, no softmax), with near-constant and with random full-mantissa
@@ -256,9 +272,7 @@ def bench_cross(vd, torch, iters: int = 20):
     d = w.draw()
     q, k, v = (_dev(d[n]) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
-    for _ in range(3):
-        vd.attn_cross(q, k, v, out=o)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: vd.attn_cross(q, k, v, out=o))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):
@@ -284,9 +298,7 @@ def bench_full_720p(vd, torch, iters: int = 5):
     q, k, v = (torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
                for _ in range(3))
     o = torch.empty_like(q)
-    for _ in range(2):
-        vd.attn_full(q, k, v, grid, out=o)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: vd.attn_full(q, k, v, grid, out=o), at_least=2)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):
@@ -319,9 +331,7 @@ def bench_window(vd, torch, iters: int = 20):
     d = w.draw_qkv()
     q, k, v = (_dev(d[n]) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
-    for _ in range(3):
-        vd.attn_window(q, k, v, grid, w.window, out=o)
-    torch.cuda.synchronize()
+    _warm(torch, lambda: vd.attn_window(q, k, v, grid, w.window, out=o))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):
@@ -359,9 +369,7 @@ def bench_qkv(vd, torch, iters: int = 20):
     def run():
         vd.qkv_proj(x, wt, b, gq, gk, grid=grid, heads=w.heads, head_dim=w.head_dim, split=w.rope_split, out=out)
 
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
+    _warm(torch, run)
     a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(iters):

@@ -35,10 +35,10 @@ def load_probe_library(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def mfma_rate(random_operands: bool, launches: int = 4, warmup: int = 2, iters: int = 10000,
+def mfma_rate(random_operands: bool, launches: int = 4, warmup: int = 8, iters: int = 10000,
               nblocks: int = 2048) -> dict:
-    """Sustained v_mfma_f32_32x32x16_bf16 rate over `launches` timed launches
-    (after `warmup` untimed ones, which also let the clock settle)."""
+    """Sustained v_mfma_f32_32x32x16_bf16 rate over `launches` timed launches,
+    after `warmup` untimed ones (~100 ms, which lets the clock settle)."""
     import torch
 
     lib = load_probe_library()
