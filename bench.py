@@ -224,6 +224,7 @@ def main():
         "cpu_baseline": None,
     }
 
+    result["temporal_alone"] = bench_temporal_alone(vd, torch, qd, kd, vd_, ot, grid, b_temporal)
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch)}
     if args.with_720p:
@@ -262,6 +263,22 @@ def mfma_ceiling(achieved_full: float):
            "near_constant": probe.mfma_rate(False), "random": probe.mfma_rate(True)}
     out["full_over_random"] = achieved_full / out["random"]["tflops"]
     return out
+
+
+def bench_temporal_alone(vd, torch, q, k, v, o, grid, nbytes, iters: int = 20):
+    """The temporal pass repeated on its own over the step's batch-2 tensors.
+    Inside the step it follows the spatial pass on the same Q/K/V, so part of
+    its reads can come from the 256 MB Infinity Cache; alone, its 805 MB
+    working set cycles through that cache with little reuse."""
+    _warm(torch, lambda: vd.attn_temporal(q, k, v, grid, out=o))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        vd.attn_temporal(q, k, v, grid, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    return {"ms": ms, "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
 
 
 def bench_cross(vd, torch, iters: int = 20):
