@@ -43,6 +43,13 @@
 //    all-VALU phase (the current tile's softmax), with a workgroup barrier
 //    after every phase, and waves 4..7 run one phase behind waves 0..3, so
 //    one wave's exponentials always run under the other's matrix products.
+//  * The other passes (4 wavefronts, two workgroups per compute unit) run
+//    each tile as a pipeline over its two 32-key blocks inside the wave:
+//    S^T of the second block between the first block's exponentials, and
+//    V^T P^T of the first block between the second's. Their two K/V buffer
+//    pairs live in two distinct LDS arrays, so the compiler can see that the
+//    transposed V reads of one pair do not alias the loads filling the other
+//    and does not wait for those loads before the reads.
 //  * The reference maximum of the online softmax is raised lazily: a tile's
 //    probabilities are formed against the current reference, and only when
 //    a lane's tile sum exceeds 2^32 (or is not finite, as on the first tile)
@@ -133,7 +140,8 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The three parts of one 64-key tile. flash_s forms S^T = K Q^T for both
+// The three parts of one 64-key tile, which the full pass's ping-pong
+// phases issue separately. flash_s forms S^T = K Q^T for both
 // 32-key blocks from the K tile at LDS byte offset KB0; flash_softmax takes
 // the online softmax over those scores (kvalid = number of the tile's keys
 // that exist) and leaves the probabilities P^T as bf16 MFMA operands;
@@ -284,20 +292,149 @@ __device__ __forceinline__ void flash_pv(const lds_u8 *lds, uint32_t VB0, const 
     }
 }
 
-// One whole 64-key tile whose K tile sits at LDS byte offset B0 and its V
-// tile at B0 + TILE. after_s() runs once the S^T products are issued.
-template <int D, int QB, typename AfterS>
-__device__ __forceinline__ void flash_tile(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
-                                           const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[QB][D / 16],
-                                           f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
-                                           float c, int kvalid, int half, AfterS after_s)
+// One 64-key tile of the 4-wave passes, as a pipeline over its two 32-key
+// blocks inside one wave: S^T of block 1 is issued between the softmax
+// steps of block 0, and V^T P^T of block 0 between those of block 1, so the
+// wave's own exponentials run under its own matrix products. The lazy
+// reference of flash_softmax is kept per block: a block whose probabilities
+// against the current reference sum past the budget (or are not finite)
+// raises it, rescales O^T and the running sum (which already hold the
+// earlier blocks) and forms that block again.
+template <int D>
+__device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
+                                                const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[1][D / 16],
+                                                f32x16 (&oacc)[D / 32][1], float (&mref)[1], float (&lsum)[1],
+                                                float c, int kvalid, int half)
 {
-    f32x16 sacc[2][QB];
-    bf16x8 pop[QB][2][2];
-    flash_s<D, QB>(lds, B0, kofs, qop, sacc);
-    after_s();
-    flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, kvalid, half);
-    flash_pv<D, QB>(lds, B0 + kBN * D * 2, vofs, pop, oacc);
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int RB = D * 2;
+    constexpr int TILE = kBN * RB;
+    f32x16 sb[2] = {(f32x16){}, (f32x16){}};
+    bf16x8 pb[2][2];
+    auto kread = [&](int kb2, int ks) {
+        return *(const __attribute__((address_space(3))) bf16x8 *)(lds + kofs[ks] + (B0 + kb2 * 32 * RB));
+    };
+    // V^T operand of 16-key step st and feature block db.
+    auto vread = [&](int st, int db) {
+        const uint32_t off = B0 + TILE + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
+        const bf16x4 lo = lds_read_tr(lds + (vofs[db] - TILE) + off);
+        const bf16x4 hi = lds_read_tr(lds + (vofs[db] - TILE) + (off + 8 * RB));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto mask = [&](int kb2) {
+        if (kvalid < kBN) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (key >= kvalid) sb[kb2][r] = -INFINITY;
+            }
+        }
+    };
+    // Probabilities r in [i*n, (i+1)*n) of block kb2 against the current reference.
+    float p[16];
+    auto prob_slice = [&](int kb2, int i, int n) {
+        const float nm = -mref[0];
+#pragma unroll
+        for (int r = i * n; r < (i + 1) * n; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(sb[kb2][r], c, nm));
+    };
+    // Sum and pack block kb2's probabilities; if the sum leaves the budget,
+    // raise the reference and form them again.
+    auto finish_block = [&](int kb2) {
+        auto sum_pack = [&]() {
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+            const float ls = (t[0] + t[1]) + (t[2] + t[3]);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                u32x4 pk;
+                pk[0] = pack_bf16x2(p[8 * s2 + 0], p[8 * s2 + 1]);
+                pk[1] = pack_bf16x2(p[8 * s2 + 2], p[8 * s2 + 3]);
+                pk[2] = pack_bf16x2(p[8 * s2 + 4], p[8 * s2 + 5]);
+                pk[3] = pack_bf16x2(p[8 * s2 + 6], p[8 * s2 + 7]);
+                pb[kb2][s2] = __builtin_bit_cast(bf16x8, pk);
+            }
+            return ls;
+        };
+        float ls = sum_pack();
+        if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
+            float mx = sb[kb2][0];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[kb2][r]);
+            mx = pair_max(mx) * c;
+            const float mnew = fmaxf(mx, mref[0]);
+            const float alpha = __builtin_amdgcn_exp2f(mref[0] - mnew);
+            mref[0] = mnew;
+            lsum[0] *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db][0] *= alpha;
+            prob_slice(kb2, 0, 16);
+            ls = sum_pack();
+        }
+        lsum[0] += ls;
+    };
+
+    // Stage 1: S^T of block 0.
+    {
+        bf16x8 ka[2];
+        ka[0] = kread(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) ka[(ks + 1) & 1] = kread(0, ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            sb[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qop[0][ks], sb[0], 0, 0, 0);
+        }
+    }
+    mask(0);
+    // Stage 2: S^T of block 1 under block 0's exponentials.
+    {
+        constexpr int n = 16 / KS;
+        bf16x8 ka[2];
+        ka[0] = kread(1, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) ka[(ks + 1) & 1] = kread(1, ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            sb[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 1], qop[0][ks], sb[1], 0, 0, 0);
+            prob_slice(0, ks, n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    finish_block(0);
+    mask(1);
+    // Stage 3: V^T P^T of block 0 (steps 0, 1) under block 1's exponentials.
+    {
+        constexpr int NM = 2 * DB;
+        constexpr int n = 16 / NM;
+        bf16x8 va[2];
+        va[0] = vread(0, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int st = m / DB, db = m % DB;
+            if (m + 1 < NM) va[(m + 1) & 1] = vread((m + 1) / DB, (m + 1) % DB);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m & 1], pb[0][st], oacc[db][0], 0, 0, 0);
+            prob_slice(1, m, n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    finish_block(1);
+    // Stage 4: V^T P^T of block 1 (steps 2, 3).
+    {
+        constexpr int NM = 2 * DB;
+        bf16x8 va[2];
+        va[0] = vread(2, 0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int st = 2 + m / DB, db = m % DB;
+            if (m + 1 < NM) va[(m + 1) & 1] = vread(2 + (m + 1) / DB, (m + 1) % DB);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m & 1], pb[1][st - 2], oacc[db][0], 0, 0, 0);
+        }
+    }
 }
 
 // PASS (0 full, 1 spatial, 2 cross, 3 window) names the instantiation, so
@@ -317,8 +454,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // The full pass (8 waves) runs two 4-wave groups out of phase over three
     // K and three V buffers; the other passes alternate two K/V pairs.
     constexpr bool PP = NW == 8 && !WIN;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[(PP ? 6 : 4) * S::TILE];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[(PP ? 6 : 2) * S::TILE];
+    // The other passes keep their second K/V buffer pair in an array of its
+    // own. With the two pairs in distinct arrays the compiler can tell that
+    // the transposed V reads of one pair do not alias the LDS-direct loads
+    // filling the other, and adds no wait for those loads before the reads.
+    __shared__ __attribute__((aligned(16))) unsigned char smem1[PP ? 16 : 2 * S::TILE];
     lds_u8 *lds = (lds_u8 *)smem;
+    lds_u8 *lds1 = (lds_u8 *)smem1;
 
     const int nqb = WIN ? wg.nqb : (L + S::BM - 1) / S::BM;
     const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)nseg * (uint32_t)heads * (uint32_t)nqb);
@@ -433,7 +576,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     }
     const uint32_t rsb = (uint32_t)(rs * 2), HWb = (uint32_t)HWt * rsb, Wpb = (uint32_t)Wpt * rsb;
     auto load_tile = [&](int t0, int buf) {
-        lds_u8 *kb = lds + buf * 2 * S::TILE;
+        lds_u8 *kb = buf ? lds1 : lds;
         lds_u8 *vb = kb + S::TILE;
         if constexpr (WIN) {
 #pragma unroll
@@ -510,8 +653,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const int ntiles = (Lk + kBN - 1) / kBN;
 
     auto tile = [&](auto bufc, int j) {
-        constexpr uint32_t B0 = decltype(bufc)::value * 2 * S::TILE;
-        flash_tile<D, QB>(lds, B0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - j * kBN, half, [] {});
+        static_assert(PP || QB == 1, "the pipelined tile holds one 32-query block per wave");
+        flash_tile_pipe<D>(decltype(bufc)::value ? lds1 : lds, 0, kofs, vofs, qop, oacc, mref, lsum, c,
+                           Lk - j * kBN, half);
     };
 
     if constexpr (PP) {
@@ -577,18 +721,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
             const uint32_t off = qi < L ? (uint32_t)((int64_t)tok(qi) * rs * 2) +
                                               (uint32_t)(((lane % S::CH) ^ swz_k<D>(r, 0)) * 16)
                                         : 0x80000000u;
-            const uint32_t dst = (i < S::LOADS ? 2 : 3) * S::TILE + (wave * S::LOADS + i % S::LOADS) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(lds + dst), 16, off, 0, 0, 0);
+            const uint32_t dst = (i < S::LOADS ? 0 : 1) * S::TILE + (wave * S::LOADS + i % S::LOADS) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(lds1 + dst), 16, off, 0, 0, 0);
         }
     }
     load_tile(0, 0);
     wait_vmem();
     __syncthreads();
     if constexpr (QSTAGE) {
-        const uint32_t qb0 = (col < 16 ? 2 * S::TILE : 3 * S::TILE - 16 * D * 2) + wave * S::LOADS * 1024;
+        const uint32_t qb0 = (col < 16 ? 0 : S::TILE - 16 * D * 2) + wave * S::LOADS * 1024;
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks)
-            qop[0][ks] = *(const __attribute__((address_space(3))) bf16x8 *)(lds + qb0 + kofs[ks]);
+            qop[0][ks] = *(const __attribute__((address_space(3))) bf16x8 *)(lds1 + qb0 + kofs[ks]);
         // The first tile-1 load below overwrites these bytes.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
@@ -616,8 +760,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // contiguous rows instead of 16-byte pieces of 32.
     {
         constexpr int OP = D * 2 + 16;  // staging pitch (bytes): rows 16 bytes apart in the banks
-        static_assert(NW * 32 * OP <= (PP ? 6 : 4) * S::TILE, "staging fits the K/V buffers");
-        lds_u8 *st = lds + wave * 32 * OP;
+        static_assert(PP ? NW * 32 * OP <= 6 * S::TILE : 2 * 32 * OP <= 2 * S::TILE, "staging fits the K/V buffers");
+        lds_u8 *st = PP ? lds + wave * 32 * OP : (wave < 2 ? lds : lds1) + (wave & 1) * 32 * OP;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const float inv = 1.0f / pair_sum(lsum[qb]);
