@@ -177,7 +177,13 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
         wait_vmem();
         __syncthreads();
     }
-    if (kt < nk) stage(std::integral_constant<int, 0>{});
+    if (kt < nk) {
+        stage(std::integral_constant<int, 0>{});
+        // The epilogue stages through LDS that other waves may still be
+        // reading in this stage. (dim is a multiple of 128, so nk is even and
+        // this branch does not run; the barrier keeps it safe if it does.)
+        __syncthreads();
+    }
 
     // Epilogue: this wave's 128 channels are one head of one of Q, K, V.
     // Lane channels within the head: cb*32 + 8*r4 + 4*half + e, e < 4 (the
