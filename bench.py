@@ -46,9 +46,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (profiling runs)")
-    p.add_argument("--with-720p", action="store_true",
-                   help="also time full attention at 720p [1,75600,40,128] after the step (same kernel as "
-                        "the 480p full pass, so it stays out of the default run that profiles summarise)")
+    p.add_argument("--no-720p", action="store_true",
+                   help="skip the full-attention timing at the 14B-shaped 720p size [1,75600,40,128]")
     p.add_argument("--no-mfma-probe", action="store_true",
                    help="skip the matrix-core rate probe that runs after the timed steps")
     p.add_argument("--copy-probe", action="store_true",
@@ -227,7 +226,7 @@ def main():
     result["temporal_alone"] = bench_temporal_alone(vd, torch, qd, kd, vd_, ot, grid, b_temporal)
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch)}
-    if args.with_720p:
+    if not args.no_720p:
         result["full_720p"] = bench_full_720p(vd, torch)
     if not args.no_mfma_probe:
         result["mfma_ceiling"] = mfma_ceiling(achieved)
