@@ -50,6 +50,9 @@ SMALL = [
     ("first_group_only_100", 1, (4, 5, 5), 2, 128),
     # 620 tokens: three query blocks (256, 256, 108), 10 key tiles.
     ("three_blocks_620", 2, (5, 4, 31), 2, 128),
+    # head_dim 64 over several key tiles: 250-token frames (4 tiles, the
+    # last with 58 keys, so its second 32-key block is ragged).
+    ("multi_tile_d64", 1, (3, 10, 25), 2, 64),
 ]
 
 
@@ -298,7 +301,10 @@ def test_block_input_path():
 # ----------------------------------------------------------------------------
 
 CROSS_SMALL = [("cross_231x77", 2, 231, 77, 2, 128), ("cross_1000x512", 1, 1000, 512, 2, 128),
-               ("cross_d64", 1, 300, 130, 3, 64), ("cross_one_key", 2, 150, 1, 2, 128)]
+               ("cross_d64", 1, 300, 130, 3, 64), ("cross_one_key", 2, 150, 1, 2, 128),
+               # head_dim 64 over five key tiles, the last with 20 keys (a
+               # fully masked second 32-key block).
+               ("cross_d64_5tiles", 1, 400, 276, 2, 64)]
 
 
 @pytest.mark.parametrize("case", CROSS_SMALL, ids=[c[0] for c in CROSS_SMALL])
