@@ -39,7 +39,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // operands of a chunk sit in registers and the next chunk's can be
 // prefetched; 0 selects a generic path that loads W step by step.
 template <int KSC>
-__global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(512) void patchify_bf16_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ w,
                                                             const uint16_t *__restrict__ bias,
                                                             uint16_t *__restrict__ tok, PatchGeom g, int K,
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     const int arow = (Kp + 8) * 2;     // bytes per A row
     const int orow = (kOut + 8) * 2;   // bytes per output-chunk row
     lds_u8 *ol0 = (lds_u8 *)dyn_lds;
-    lds_u8 *al = ol0 + 2 * kTok * orow;
+    lds_u8 *al = ol0 + 4 * kTok * orow;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -61,8 +61,10 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     const int64_t M = (int64_t)g.B * N;
     const int64_t m0 = (int64_t)blockIdx.x * kTok;
 
-    // Gather the patch matrix (zero past K and past the last token).
-    if (g.pw == 2 && (g.Wl & 1) == 0 && kTok == 64) {
+    // Gather the patch matrix (zero past K and past the last token), with
+    // the first four wavefronts.
+    if (tid >= 256) {
+    } else if (g.pw == 2 && (g.Wl & 1) == 0 && kTok == 64) {
         // Bricks two wide (an even latent width keeps every pair 4-byte
         // aligned): lane l of each wave owns token m0 + l, and the waves take
         // the token's (c, i, j) rows in turn, one 4-byte (kw = 0, 1) pair per
@@ -131,14 +133,19 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     __syncthreads();
 
     const bool kvec = (K % 8) == 0;  // W rows can be read as 16-byte vectors
+    // Two groups of four wavefronts take alternate channel chunks: group grp
+    // does chunks c0 + grp, c0 + grp + 2, ..., each wave 32 of a chunk's 128
+    // channels, and both groups meet one barrier per step.
     // This workgroup's channel chunks: kOut-wide chunks c0, c0 + 1, ..., c1 - 1.
     const int nchunks = (g.Dout + kOut - 1) / kOut;
     const int per = (nchunks + gridDim.y - 1) / gridDim.y;
     const int c0 = blockIdx.y * per, c1 = min(nchunks, c0 + per);
+    const int grp = wave >> 2, gw = wave & 3, gtid = tid & 255;
+    const int nsteps = (c1 - c0 + 1) / 2;
     // W operands (A of C^T = W A^T) of chunk oc, step s2: lane row
     // oc + wave*32 + col, features 16*s2 + 8*half .. +8.
     auto w_op = [&](int oc, int s2) {
-        const int orow_w = oc + wave * 32 + col;
+        const int orow_w = oc + gw * 32 + col;
         const int k0 = 16 * s2 + 8 * half;
         bf16x8 v8 = (bf16x8){};
         if (orow_w < g.Dout) {
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     // 4*half .. +4, one 8-byte load each (Dout is a multiple of 8 and bias is
     // 16-byte aligned, so a run of 4 never straddles the end).
     auto b_op = [&](int oc, int r4) {
-        const int ch = oc + wave * 32 + 8 * r4 + 4 * half;
+        const int ch = oc + gw * 32 + 8 * r4 + 4 * half;
         u32x2 v = (u32x2){0u, 0u};
         if (bias && ch < g.Dout) v = *(const u32x2 *)(bias + ch);
         return v;
@@ -165,80 +172,85 @@ __global__ __launch_bounds__(256) void patchify_bf16_kernel(const uint16_t *__re
     constexpr int NS = KSC > 0 ? KSC : 1;
     bf16x8 wcur[NS], wnext[NS];
     u32x2 bcur[4], bnext[4];
-    if (c0 < c1) {
+    if (c0 + grp < c1) {
         if constexpr (KSC > 0) {
 #pragma unroll
-            for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = w_op(c0 * kOut, s2);
+            for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = w_op((c0 + grp) * kOut, s2);
         }
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = b_op(c0 * kOut, r4);
+        for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = b_op((c0 + grp) * kOut, r4);
     }
-    for (int ci = c0; ci < c1; ++ci) {
+    for (int st = 0; st < nsteps; ++st) {
+        const int ci = c0 + 2 * st + grp;
+        const bool live = ci < c1;
         const int oc = ci * kOut;
-        lds_u8 *ol = ol0 + ((ci - c0) & 1) * kTok * orow;
-        // The next chunk's bias loads are in flight during this chunk.
-        if (ci + 1 < c1)
+        lds_u8 *ol = ol0 + (2 * grp + (st & 1)) * kTok * orow;
+        if (live) {
+            // The group's next chunk's bias loads are in flight during this chunk.
+            if (ci + 2 < c1)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) bnext[r4] = b_op(oc + kOut, r4);
-        f32x16 acc[kTB];
+                for (int r4 = 0; r4 < 4; ++r4) bnext[r4] = b_op(oc + 2 * kOut, r4);
+            f32x16 acc[kTB];
 #pragma unroll
-        for (int tb = 0; tb < kTB; ++tb) acc[tb] = (f32x16){};
-        auto step = [&](int s2, const bf16x8 &wa) {
-            const int k0 = 16 * s2 + 8 * half;
+            for (int tb = 0; tb < kTB; ++tb) acc[tb] = (f32x16){};
+            auto step = [&](int s2, const bf16x8 &wa) {
+                const int k0 = 16 * s2 + 8 * half;
 #pragma unroll
-            for (int tb = 0; tb < kTB; ++tb) {
-                const bf16x8 bt = *(const __attribute__((address_space(3))) bf16x8 *)(
-                    al + (tb * 32 + col) * arow + k0 * 2);
-                acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc[tb], 0, 0, 0);
-            }
-        };
-        if constexpr (KSC > 0) {
-            // The next chunk's W loads are in flight during this chunk.
-            if (ci + 1 < c1)
-#pragma unroll
-                for (int s2 = 0; s2 < KSC; ++s2) wnext[s2] = w_op(oc + kOut, s2);
-#pragma unroll
-            for (int s2 = 0; s2 < KSC; ++s2) step(s2, wcur[s2]);
-#pragma unroll
-            for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = wnext[s2];
-        } else {
-            for (int s2 = 0; s2 < Kp / 16; ++s2) step(s2, w_op(oc, s2));
-        }
-        // acc[tb]: lane holds token tb*32+col, channels wave*32 + 8*(r/4) + 4*half + r%4.
-#pragma unroll
-        for (int tb = 0; tb < kTB; ++tb)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int oo = wave * 32 + 8 * r4 + 4 * half;  // channel within the chunk
-                float vals[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t bw = bcur[r4][e >> 1];
-                    const float bv = __uint_as_float((e & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
-                    vals[e] = acc[tb][4 * r4 + e] + bv;
+                for (int tb = 0; tb < kTB; ++tb) {
+                    const bf16x8 bt = *(const __attribute__((address_space(3))) bf16x8 *)(
+                        al + (tb * 32 + col) * arow + k0 * 2);
+                    acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bt, acc[tb], 0, 0, 0);
                 }
-                u32x2 pk;
-                pk[0] = pack_bf16x2(vals[0], vals[1]);
-                pk[1] = pack_bf16x2(vals[2], vals[3]);
-                *(__attribute__((address_space(3))) u32x2 *)(ol + (tb * 32 + col) * orow + oo * 2) = pk;
-            }
+            };
+            if constexpr (KSC > 0) {
+                // The group's next chunk's W loads are in flight during this chunk.
+                if (ci + 2 < c1)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = bnext[r4];
-        // One barrier per chunk: it orders this chunk's LDS writes before the
-        // reads below, and the previous chunk's reads of the other buffer
-        // before the next chunk's writes to it. It orders LDS only, so the
-        // global stores stay in flight across it.
+                    for (int s2 = 0; s2 < KSC; ++s2) wnext[s2] = w_op(oc + 2 * kOut, s2);
+#pragma unroll
+                for (int s2 = 0; s2 < KSC; ++s2) step(s2, wcur[s2]);
+#pragma unroll
+                for (int s2 = 0; s2 < KSC; ++s2) wcur[s2] = wnext[s2];
+            } else {
+                for (int s2 = 0; s2 < Kp / 16; ++s2) step(s2, w_op(oc, s2));
+            }
+            // acc[tb]: lane holds token tb*32+col, channels gw*32 + 8*(r/4) + 4*half + r%4.
+#pragma unroll
+            for (int tb = 0; tb < kTB; ++tb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int oo = gw * 32 + 8 * r4 + 4 * half;  // channel within the chunk
+                    float vals[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t bw = bcur[r4][e >> 1];
+                        const float bv = __uint_as_float((e & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+                        vals[e] = acc[tb][4 * r4 + e] + bv;
+                    }
+                    u32x2 pk;
+                    pk[0] = pack_bf16x2(vals[0], vals[1]);
+                    pk[1] = pack_bf16x2(vals[2], vals[3]);
+                    *(__attribute__((address_space(3))) u32x2 *)(ol + (tb * 32 + col) * orow + oo * 2) = pk;
+                }
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) bcur[r4] = bnext[r4];
+        }
+        // One barrier per step: it orders each group's LDS writes of this
+        // step before its reads below, and its reads of the step before
+        // (other buffer) ahead of its writes to that buffer in the next step.
+        // It orders LDS only, so the global stores stay in flight across it.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        for (int idx = tid; idx < kTok * (kOut / 8); idx += 256) {
-            const int r = idx / (kOut / 8), ch = idx % (kOut / 8);
-            const int64_t m = m0 + r;
-            const int o0 = oc + ch * 8;
-            if (m < M && o0 < g.Dout)
-                *(u32x4 *)(tok + m * g.Dout + o0) = *(const __attribute__((address_space(3))) u32x4 *)(
-                    ol + r * orow + ch * 16);
-        }
+        if (live)
+            for (int idx = gtid; idx < kTok * (kOut / 8); idx += 256) {
+                const int r = idx / (kOut / 8), ch = idx % (kOut / 8);
+                const int64_t m = m0 + r;
+                const int o0 = oc + ch * 8;
+                if (m < M && o0 < g.Dout)
+                    *(u32x4 *)(tok + m * g.Dout + o0) = *(const __attribute__((address_space(3))) u32x4 *)(
+                        ol + r * orow + ch * 16);
+            }
     }
 }
 
@@ -276,14 +288,14 @@ hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, 
     if (Kp > kMaxK || g.Dout % 8) return hipErrorInvalidValue;
     const int64_t M = (int64_t)g.B * g.T * g.Hp * g.Wp;
     const dim3 grid((uint32_t)((M + kTok - 1) / kTok), kChunkSplit);
-    const size_t lds = (size_t)kTok * (2 * (kOut + 8) + (Kp + 8)) * 2;
+    const size_t lds = (size_t)kTok * (4 * (kOut + 8) + (Kp + 8)) * 2;
     auto go = [&](auto kernel) {
         if (lds > 65536) {  // above the default dynamic-LDS limit (up to 99 KB at Kp = 512)
             const hipError_t e =
                 hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(kernel, grid, dim3(256), lds, s, (const uint16_t *)x, (const uint16_t *)w,
+        hipLaunchKernelGGL(kernel, grid, dim3(512), lds, s, (const uint16_t *)x, (const uint16_t *)w,
                            (const uint16_t *)bias, (uint16_t *)tok, g, K, Kp);
         return hipGetLastError();
     };
