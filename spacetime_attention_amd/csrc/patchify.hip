@@ -61,10 +61,12 @@ __global__ __launch_bounds__(512) void patchify_bf16_kernel(const uint16_t *__re
     const int64_t M = (int64_t)g.B * N;
     const int64_t m0 = (int64_t)blockIdx.x * kTok;
 
-    // Gather the patch matrix (zero past K and past the last token), with
-    // the first four wavefronts.
-    if (tid >= 256) {
-    } else if (g.pw == 2 && (g.Wl & 1) == 0 && kTok == 64) {
+    // Gather the patch matrix (zero past K and past the last token): all
+    // eight wavefronts on the fast path for two-wide bricks, the first four
+    // on the general one.
+    const bool fast_gather = g.pw == 2 && (g.Wl & 1) == 0 && kTok == 64;
+    if (!fast_gather && tid >= 256) {
+    } else if (fast_gather) {
         // Bricks two wide (an even latent width keeps every pair 4-byte
         // aligned): lane l of each wave owns token m0 + l, and the waves take
         // the token's (c, i, j) rows in turn, one 4-byte (kw = 0, 1) pair per
@@ -79,17 +81,17 @@ __global__ __launch_bounds__(512) void patchify_bf16_kernel(const uint16_t *__re
             const int hh = (int)((n / g.Wp) % g.Hp), ww = (int)(n % g.Wp);
             const uint16_t *xb = x + (((b * g.C) * g.Tl + (int64_t)t * g.pt) * g.Hl + (int64_t)hh * g.ph) * g.Wl +
                                  (int64_t)ww * 2;
-            for (int cij = wave; cij < rows; cij += 4) {
+            for (int cij = wave; cij < rows; cij += 8) {
                 const int j = cij % g.ph, i = (cij / g.ph) % g.pt, c = cij / (g.ph * g.pt);
                 const uint32_t v2 = *(const uint32_t *)(xb + (((int64_t)c * g.Tl + i) * g.Hl + j) * g.Wl);
                 *(__attribute__((address_space(3))) uint32_t *)(arow_p + cij * 4) = v2;
             }
         } else {
-            for (int cij = wave; cij < rows; cij += 4)
+            for (int cij = wave; cij < rows; cij += 8)
                 *(__attribute__((address_space(3))) uint32_t *)(arow_p + cij * 4) = 0u;
         }
         // Padding columns K .. Kp-1 (K is even here).
-        for (int kk = K + 2 * wave; kk < Kp; kk += 8)
+        for (int kk = K + 2 * wave; kk < Kp; kk += 16)
             *(__attribute__((address_space(3))) uint32_t *)(arow_p + kk * 2) = 0u;
     } else {
         // Any brick: each thread owns one token and a run of KR = Kp / (256 /
