@@ -206,6 +206,19 @@ def test_patchify_small(dtype):
     assert_close(got, ref, dtype, f"patchify/{dtype}")
 
 
+def test_patchify_general_gather_chunks():
+    # Three-wide bricks take the general gather; 384 output channels are three
+    # 128-channel chunks, so both chunk groups of a workgroup work, the first
+    # group twice.
+    _announce("patchify general gather, 3 chunks")
+    d = draw(43, [("x", (2, 4, 4, 7, 9), 1.0), ("w", (384, 4, 2, 2, 3), 0.02), ("b", (384,), 0.1)], "bf16")
+    x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
+    got = to_host(vd.patchify(x, wt, b, heads=3, head_dim=128))
+    ref = oracle.patchify(d["x"].f32, d["w"].f32, d["b"].f32)
+    assert got.shape == ref.shape == (2, 2 * 3 * 3, 384)
+    assert_close(got, ref, "bf16", "patchify/general/3 chunks")
+
+
 @pytest.mark.parametrize("C,dout", [(16, 384), (12, 640), (16, 1536)])
 def test_patchify_bias_chunks(C, dout):
     # Several 128-channel chunks with a bias (each chunk's bias is fetched
