@@ -225,7 +225,9 @@ def main():
 
     result["temporal_alone"] = bench_temporal_alone(vd, torch, qd, kd, vd_, ot, grid, b_temporal)
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
-                           "qkv_proj": bench_qkv(vd, torch)}
+                           "qkv_proj": bench_qkv(vd, torch),
+                           "rope_in_attention": bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_,
+                                                                        os_, grid, f_full, f_spatial)}
     if not args.no_720p:
         result["full_720p"] = bench_full_720p(vd, torch)
     if not args.no_mfma_probe:
@@ -358,6 +360,51 @@ def bench_window(vd, torch, iters: int = 20):
     flop = window_flop(w, w.window)
     return {"workload": f"[{w.B},{w.N},{w.heads},{w.head_dim}] grid {grid} windows {w.window}",
             "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
+
+
+def bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_, od, grid, f_full, f_spatial,
+                            rounds: int = 3, iters: int = 10):
+    """RoPE applied inside the attention kernel against the separate RoPE
+    pass on Q and on K followed by the plain kernel, on the step's full
+    (batch 1) and spatial (batch 2) inputs, timed on their own after the
+    step in alternating blocks of `iters` launches so that both see the same
+    clock. The FLOP rates count only the attention product."""
+    split = (44, 42, 42)
+
+    def sep(q, k, v, o, attn):
+        qr, kr = torch.empty_like(q), torch.empty_like(k)
+
+        def run():
+            vd.rope3d(q, grid, split, out=qr)
+            vd.rope3d(k, grid, split, out=kr)
+            attn(qr, kr, v, grid, out=o)
+        return run
+
+    out = {}
+    for name, q, k, v, o, plain, fused, flop in (
+            ("full", qf, kf, vf, of, vd.attn_full, vd.attn_full_rope, f_full),
+            ("spatial", qd, kd, vd_, od, vd.attn_spatial, vd.attn_spatial_rope, f_spatial)):
+        runs = {"fused": lambda: fused(q, k, v, grid, split, out=o), "separate": sep(q, k, v, o, plain)}
+        ms = {key: [] for key in runs}
+        for key, fn in runs.items():
+            _warm(torch, fn)
+        for _ in range(rounds):
+            for key, fn in runs.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(iters):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                ms[key].append(a.elapsed_time(b) / iters)
+        med = {key: float(np.median(v_)) for key, v_ in ms.items()}
+        out[name] = {"fused_ms": med["fused"], "separate_ms": med["separate"],
+                     "fused_tflops": flop / med["fused"] / 1e9,
+                     "fused_over_separate": med["fused"] / med["separate"]}
+        del runs
+    out["workload"] = f"480p grid {grid}, 12 heads x 128, split {split}: full [1,32760,12,128], " \
+                      f"spatial [2,32760,12,128]; separate = vdit_rope3d on q and on k, then the plain pass"
+    return out
 
 
 def _cpu_model() -> str:

@@ -1,7 +1,7 @@
 /*
  * vdit.h — C ABI of the spacetime-attention library (libvdit.so), gfx950.
  *
- * Five operations of a video diffusion transformer's self-attention input
+ * The operations of a video diffusion transformer's self-attention input
  * path, each enqueued on a caller-supplied HIP stream:
  *
  *   vdit_patchify       Conv3d with stride = kernel, as a GEMM, to token-major
@@ -10,6 +10,9 @@
  *   vdit_attn_full      softmax attention over all T*Hp*Wp tokens of a clip;
  *   vdit_attn_spatial   the same, with keys limited to the query's own latent
  *                       frame;
+ *   vdit_attn_full_rope, vdit_attn_spatial_rope
+ *                       the two above with 3D RoPE applied to q and k inside
+ *                       the attention kernel (no separate RoPE pass);
  *   vdit_attn_temporal  the same, with keys limited to the query's own patch
  *                       position across frames;
  *   vdit_attn_cross     attention from the video tokens to another token set
@@ -162,6 +165,34 @@ vdit_status_t vdit_attn_full(const void *q, const void *k, const void *v, void *
 vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, void *o,
                                 int B, int heads, int T, int Hp, int Wp, int head_dim,
                                 float scale, vdit_dtype_t dtype, void *stream);
+
+/*
+ * vdit_attn_full_rope, vdit_attn_spatial_rope — full or spatial attention of
+ * the rotated queries and keys: the result equals vdit_rope3d on q and on k
+ * (same d_t, d_h, d_w, theta) followed by vdit_attn_full or
+ * vdit_attn_spatial, without the rotated copies ever reaching memory. In Wan
+ * 2.1's attn1 ("How AI Generates Video ...", section 5) the rotation is the
+ * step right before the attention product; here the kernel applies it to the
+ * queries once after reading them and to every K tile as it arrives in
+ * on-chip memory, so it is repeated once per query block that reads the
+ * tile. q and k in memory are not modified.
+ *
+ * Arguments, layouts, limits and errors as vdit_attn_full, plus d_t, d_h,
+ * d_w and theta as vdit_rope3d (VDIT_E_ROPE_SPLIT for a bad split,
+ * VDIT_E_SHAPE for theta <= 0 or not finite). The angle of each pair is
+ * formed in fp32 in revolutions and its sin/cos taken by the hardware's
+ * v_sin_f32/v_cos_f32; the rotated q and k are rounded to bf16, as
+ * vdit_rope3d's output is. dtype: VDIT_BF16 only (VDIT_F32 gives
+ * VDIT_E_DTYPE: the fp32 parity path is vdit_rope3d then the plain call).
+ */
+vdit_status_t vdit_attn_full_rope(const void *q, const void *k, const void *v, void *o,
+                                  int B, int heads, int T, int Hp, int Wp, int head_dim,
+                                  int d_t, int d_h, int d_w, float theta, float scale,
+                                  vdit_dtype_t dtype, void *stream);
+vdit_status_t vdit_attn_spatial_rope(const void *q, const void *k, const void *v, void *o,
+                                     int B, int heads, int T, int Hp, int Wp, int head_dim,
+                                     int d_t, int d_h, int d_w, float theta, float scale,
+                                     vdit_dtype_t dtype, void *stream);
 
 /*
  * vdit_attn_temporal — the temporal pass of divided attention.

@@ -13,8 +13,12 @@ Functions (names as in the C ABI, without the ``vdit_`` prefix):
   rope3d(x, grid, split=(44, 42, 42), theta=10000.0, out=None)
   attn_full(q, k, v, grid, scale=0.0, out=None)
   attn_spatial(q, k, v, grid, scale=0.0, out=None)
+  attn_full_rope(q, k, v, grid, split=(44, 42, 42), theta=10000.0, scale=0.0, out=None)
+  attn_spatial_rope(q, k, v, grid, split=(44, 42, 42), theta=10000.0, scale=0.0, out=None)
   attn_temporal(q, k, v, grid, scale=0.0, out=None)
   attn_cross(q, k, v, scale=0.0, out=None)
+  attn_window(q, k, v, grid, window, scale=0.0, out=None)
+  qkv_proj(x, w, bias=None, gamma_q=None, gamma_k=None, *, grid, heads, head_dim, ...)
 Token tensors are ``[B, N, heads, head_dim]`` with ``N = T*Hp*Wp`` and token
 ``(t, h, w)`` at ``n = (t*Hp + h)*Wp + w``; ``grid = (T, Hp, Wp)``.
 """
@@ -34,8 +38,8 @@ BF16, F32 = 0, 1
 STATUS = ["VDIT_OK", "VDIT_E_NULL", "VDIT_E_SHAPE", "VDIT_E_HEAD_DIM", "VDIT_E_ROPE_SPLIT",
           "VDIT_E_ALIGN", "VDIT_E_ALIAS", "VDIT_E_DTYPE", "VDIT_E_LAUNCH"]
 EXPORTS = ("vdit_status_str", "vdit_patchify", "vdit_rope3d", "vdit_attn_full",
-           "vdit_attn_spatial", "vdit_attn_temporal", "vdit_attn_cross", "vdit_attn_window",
-           "vdit_qkv_proj")
+           "vdit_attn_spatial", "vdit_attn_full_rope", "vdit_attn_spatial_rope", "vdit_attn_temporal",
+           "vdit_attn_cross", "vdit_attn_window", "vdit_qkv_proj")
 
 
 class VditError(RuntimeError):
@@ -67,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("vdit_attn_full", "vdit_attn_spatial", "vdit_attn_temporal"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp] + [i] * 6 + [f, i, vp]
+        fn.restype = i
+    for name in ("vdit_attn_full_rope", "vdit_attn_spatial_rope"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp] + [i] * 9 + [f, f, i, vp]
         fn.restype = i
     lib.vdit_attn_cross.argtypes = [vp, vp, vp, vp] + [i] * 5 + [f, i, vp]
     lib.vdit_attn_cross.restype = i
@@ -178,6 +186,39 @@ def attn_full(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:
 def attn_spatial(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:
     """Attention within each latent frame."""
     return _attn("vdit_attn_spatial", q, k, v, grid, scale, out)
+
+
+def _attn_rope(fn_name: str, q, k, v, grid, split, theta, scale, out):
+    B, N, heads, D = q.shape
+    T, Hp, Wp = grid
+    if N != T * Hp * Wp:
+        raise ValueError("token count does not match the grid")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out has the wrong shape")
+    d_t, d_h, d_w = (int(a) for a in split)
+    lib = load_library()
+    dt = q.dtype
+    _check(getattr(lib, fn_name)(_dev(q, "q"), _dev(k, "k", dt), _dev(v, "v", dt), _dev(out, "out", dt),
+                                 B, heads, T, Hp, Wp, D, d_t, d_h, d_w, float(theta), float(scale),
+                                 _dtype_code(q), _stream(q)))
+    return out
+
+
+def attn_full_rope(q, k, v, grid, split: Sequence[int] = (44, 42, 42), theta: float = 10000.0,
+                   scale: float = 0.0, out=None) -> torch.Tensor:
+    """Full attention of RoPE(q) against RoPE(k), rotated inside the kernel
+    (q and k stay unrotated in memory)."""
+    return _attn_rope("vdit_attn_full_rope", q, k, v, grid, split, theta, scale, out)
+
+
+def attn_spatial_rope(q, k, v, grid, split: Sequence[int] = (44, 42, 42), theta: float = 10000.0,
+                      scale: float = 0.0, out=None) -> torch.Tensor:
+    """Spatial attention of RoPE(q) against RoPE(k), rotated inside the kernel."""
+    return _attn_rope("vdit_attn_spatial_rope", q, k, v, grid, split, theta, scale, out)
 
 
 def attn_temporal(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:

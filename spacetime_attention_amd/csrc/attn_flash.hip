@@ -140,6 +140,28 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// RoPE on one 16-byte chunk of a head vector: its eight bf16 values are
+// logical chunk lc, i.e. pairs 4*lc .. 4*lc+3, of a token at grid position
+// (pt, ph, pw). The angle is taken in revolutions and reduced to [0, 1)
+// for v_sin_f32 / v_cos_f32; rtab holds the pairs' frequencies.
+__device__ __forceinline__ u32x4 rope_chunk(u32x4 x, int lc, float pt, float ph, float pw, const lds_f32 *rtab,
+                                            int b1, int b2)
+{
+    const f32x4 fq = *(const __attribute__((address_space(3))) f32x4 *)(rtab + 4 * lc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int p = 4 * lc + e;
+        const float pos = p < b1 ? pt : (p < b2 ? ph : pw);
+        const float rev = __builtin_amdgcn_fractf(pos * fq[e]);
+        const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+        const float x0 = __uint_as_float(x[e] << 16), x1 = __uint_as_float(x[e] & 0xffff0000u);
+        x[e] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+    }
+    return x;
+}
+
 // The three parts of one 64-key tile, which the full pass's ping-pong
 // phases issue separately. flash_s forms S^T = K Q^T for both
 // 32-key blocks from the K tile at LDS byte offset KB0; flash_softmax takes
@@ -437,16 +459,20 @@ __device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, 
     }
 }
 
-// PASS (0 full, 1 spatial, 2 cross, 3 window) names the instantiation, so
-// that profiles attribute the passes separately; the first three run the
-// same code. L is the number of queries and Lk the number of keys per
+// PASS (0 full, 1 spatial, 2 cross, 3 window, 4 full with RoPE, 5 spatial
+// with RoPE) names the instantiation, so that profiles attribute the passes
+// separately; the first three run the same code. The RoPE passes rotate the
+// queries in registers after they are read, and each wave rotates its own
+// share of every K tile in LDS once its loads of that tile have landed and
+// before the barrier that hands the tile to the other waves, so the barrier
+// protocol is the same as without RoPE. L is the number of queries and Lk the number of keys per
 // segment (equal for self-attention; the text length for cross-attention);
 // the window pass takes both from the window it works on and nseg = B times
 // the number of windows.
 template <int D, int QB, int NW, int PASS>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    uint16_t *__restrict__ o, int nseg, int L, int Lk, int heads, float c, WinGeom wg)
+    uint16_t *__restrict__ o, int nseg, int L, int Lk, int heads, float c, WinGeom wg, FlashRope fr)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     using S = FlashShape<D, QB, NW>;
@@ -459,9 +485,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // own. With the two pairs in distinct arrays the compiler can tell that
     // the transposed V reads of one pair do not alias the LDS-direct loads
     // filling the other, and adds no wait for those loads before the reads.
-    __shared__ __attribute__((aligned(16))) unsigned char smem1[PP ? 16 : 2 * S::TILE];
+    // The RoPE passes keep their 64 pair frequencies after it.
+    constexpr bool ROPE = PASS >= 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem1[(PP ? 0 : 2 * S::TILE) + (ROPE ? 256 : (PP ? 16 : 0))];
     lds_u8 *lds = (lds_u8 *)smem;
     lds_u8 *lds1 = (lds_u8 *)smem1;
+    lds_f32 *rtab = (lds_f32 *)(lds1 + (PP ? 0 : 2 * S::TILE));
+    if constexpr (ROPE) {
+        if (threadIdx.x < D / 2) rtab[threadIdx.x] = fr.freq_rev[threadIdx.x];
+        __syncthreads();
+    }
 
     const int nqb = WIN ? wg.nqb : (L + S::BM - 1) / S::BM;
     const uint32_t id = xcd_contiguous(blockIdx.x, (uint32_t)nseg * (uint32_t)heads * (uint32_t)nqb);
@@ -519,6 +552,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // The 4-wave passes stage the queries through LDS (below); the full pass
     // reads them straight into registers, once for its whole key loop.
     constexpr bool QSTAGE = !PP && QB == 1 && NW == 4;
+    // RoPE: token rows are batch-major, so a row's index within its clip
+    // (and with it the row's grid position) is the row modulo T*Hp*Wp.
+    const int HWg = fr.Hp * fr.Wp;
+    const int64_t Ng = (int64_t)fr.T * HWg;
+    auto rope_q = [&]() {
+        const int n = (int)((qorg + q0 + col) % Ng);
+        const float pt = (float)(n / HWg), ph = (float)((n / fr.Wp) % fr.Hp), pw = (float)(n % fr.Wp);
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks)
+            qop[0][ks] = __builtin_bit_cast(
+                bf16x8, rope_chunk(__builtin_bit_cast(u32x4, qop[0][ks]), 2 * ks + half, pt, ph, pw, rtab, fr.b1,
+                                   fr.b2));
+    };
     if constexpr (!QSTAGE) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -532,6 +578,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
                     qop[qb][ks] = (bf16x8){};
             }
         }
+        if constexpr (ROPE) rope_q();
     }
 
     // Buffer descriptors over this (segment, head)'s keys and values: the
@@ -575,6 +622,44 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         }
     }
     const uint32_t rsb = (uint32_t)(rs * 2), HWb = (uint32_t)HWt * rsb, Wpb = (uint32_t)Wpt * rsb;
+    // RoPE: grid position (rt, rh, rw) of the key row each of this wave's
+    // loads fills in the next K tile to be rotated. Tiles are rotated in
+    // order, and one tile step adds 64 = rdt*Hp*Wp + rdh*Wp + rdw with single
+    // carries, as for the window digits above.
+    int rt[S::LOADS], rh[S::LOADS], rw[S::LOADS];
+    int rdt = 0, rdh = 0, rdw = 0;
+    if constexpr (ROPE) {
+        rdt = kBN / HWg;
+        rdh = (kBN % HWg) / fr.Wp;
+        rdw = kBN % fr.Wp;
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int r = RPL * (wave * S::LOADS + i) + lane / S::CH;
+            const int n = (int)((korg + r) % Ng);
+            rt[i] = n / HWg;
+            rh[i] = (n / fr.Wp) % fr.Hp;
+            rw[i] = n % fr.Wp;
+        }
+    }
+    // Rotates this wave's share of the K tile at kb: each lane rewrites the
+    // 16 bytes its own load wrote (row r, physical chunk lane % CH, which
+    // holds logical chunk (lane % CH) ^ (r % CH)).
+    auto rope_k = [&](lds_u8 *kb) {
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int r = RPL * (wave * S::LOADS + i) + lane / S::CH;
+            const int lc = (lane % S::CH) ^ (r % S::CH);
+            auto *p = (__attribute__((address_space(3))) u32x4 *)(kb + (wave * S::LOADS + i) * 1024 + 16 * lane);
+            *p = rope_chunk(*p, lc, (float)rt[i], (float)rh[i], (float)rw[i], rtab, fr.b1, fr.b2);
+            rw[i] += rdw;
+            const int cw1 = rw[i] >= fr.Wp;
+            rw[i] -= cw1 ? fr.Wp : 0;
+            rh[i] += rdh + cw1;
+            const int ch1 = rh[i] >= fr.Hp;
+            rh[i] -= ch1 ? fr.Hp : 0;
+            rt[i] += rdt + ch1;
+        }
+    };
     auto load_tile = [&](int t0, int buf) {
         lds_u8 *kb = buf ? lds1 : lds;
         lds_u8 *vb = kb + S::TILE;
@@ -679,6 +764,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         if (ntiles > 1) load_one(krs, koff, kBN, S::TILE);
         load_one(vrs, voff, 0, VB);
         wait_vmem();
+        if constexpr (ROPE) {
+            rope_k(lds);
+            if (ntiles > 1) rope_k(lds + S::TILE);
+        }
         __syncthreads();
         if (late) lds_barrier();
         auto phase = [&](auto bufc, int j) {
@@ -696,6 +785,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
             if (j + 1 < ntiles) load_one(vrs, voff, (j + 1) * kBN, VB + b1 * S::TILE);
             if (busy) flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, Lk - j * kBN, half);
             wait_vmem();
+            if constexpr (ROPE)
+                if (j + 2 < ntiles) rope_k(lds + b2 * S::TILE);
             lds_barrier();
             return true;
         };
@@ -727,6 +818,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     }
     load_tile(0, 0);
     wait_vmem();
+    if constexpr (ROPE) rope_k(lds);
     __syncthreads();
     if constexpr (QSTAGE) {
         const uint32_t qb0 = (col < 16 ? 0 : S::TILE - 16 * D * 2) + wave * S::LOADS * 1024;
@@ -735,6 +827,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
             qop[0][ks] = *(const __attribute__((address_space(3))) bf16x8 *)(lds1 + qb0 + kofs[ks]);
         // The first tile-1 load below overwrites these bytes.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (ROPE) rope_q();
     }
     // Tiles alternate between the two LDS buffers; the loop body takes one
     // tile from each so that the buffer is a compile-time constant. The
@@ -744,11 +837,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         if (j + 1 < ntiles) load_tile((j + 1) * kBN, 1);
         if (busy) tile(std::integral_constant<int, 0>{}, j);
         wait_vmem();
+        if constexpr (ROPE)
+            if (j + 1 < ntiles) rope_k(lds1);
         __syncthreads();
         if (j + 1 >= ntiles) break;
         if (j + 2 < ntiles) load_tile((j + 2) * kBN, 0);
         if (busy) tile(std::integral_constant<int, 1>{}, j + 1);
         wait_vmem();
+        if constexpr (ROPE)
+            if (j + 2 < ntiles) rope_k(lds);
         __syncthreads();
     }
     }
@@ -795,7 +892,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
 template <int D, int QB, int NW, int PASS>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
-                  int heads, float c, hipStream_t s, WinGeom wg = WinGeom{}) {
+                  int heads, float c, hipStream_t s, WinGeom wg = WinGeom{}, FlashRope fr = FlashRope{}) {
     using S = FlashShape<D, QB, NW>;
     if (PASS == 3) {
         // L is the largest window's token count; nseg = B * windows.
@@ -806,7 +903,7 @@ hipError_t launch(const void *q, const void *k, const void *v, void *o, int nseg
     if (grid == 0 || grid > UINT32_MAX) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((flash_fwd_bf16<D, QB, NW, PASS>), dim3((uint32_t)grid), dim3(S::THREADS), 0, s,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o,
-                       nseg, L, Lk, heads, c, wg);
+                       nseg, L, Lk, heads, c, wg, fr);
     return hipGetLastError();
 }
 
@@ -823,6 +920,21 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
         if (pass == 0) return launch<64, 1, kFullWaves, 0>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
         if (pass == 1) return launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
         return launch<64, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_flash_rope_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
+                                  int heads, int D, float scale_log2e, int pass, const FlashRope &rope,
+                                  hipStream_t s) {
+    const float c = scale_log2e;
+    if (D == 128) {
+        if (pass == 0) return launch<128, 1, kFullWaves, 4>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
+        if (pass == 1) return launch<128, 1, kSpatialWaves, 5>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
+    }
+    if (D == 64) {
+        if (pass == 0) return launch<64, 1, kFullWaves, 4>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
+        if (pass == 1) return launch<64, 1, kSpatialWaves, 5>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
     }
     return hipErrorInvalidValue;
 }

@@ -34,10 +34,25 @@ vdit_status_t launch_status(hipError_t e) { return e == hipSuccess ? VDIT_OK : V
 
 enum Mode { kFull = 0, kSpatial = 1, kTemporal = 2 };
 
+// RoPE split of a head vector into (d_t, d_h, d_w): nonnegative even parts
+// that add up to head_dim.
+bool split_ok(int D, int d_t, int d_h, int d_w) {
+    return d_t >= 0 && d_h >= 0 && d_w >= 0 && !(d_t & 1) && !(d_h & 1) && !(d_w & 1) &&
+           (int64_t)d_t + d_h + d_w == D;
+}
+
+// Rotation parameters of the attention kernels that apply RoPE themselves
+// (rope != nullptr selects them; `split` = {d_t, d_h, d_w}).
+struct AttnRope {
+    int split[3];
+    float theta;
+};
+
 vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, int heads, int T, int Hp, int Wp,
-                   int D, float scale, vdit_dtype_t dt, void *stream, Mode mode) {
+                   int D, float scale, vdit_dtype_t dt, void *stream, Mode mode, const AttnRope *rope = nullptr) {
     if (!q || !k || !v || !o) return VDIT_E_NULL;
     if (dt != VDIT_BF16 && dt != VDIT_F32) return VDIT_E_DTYPE;
+    if (rope && dt != VDIT_BF16) return VDIT_E_DTYPE;
     if (B <= 0 || heads <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || D <= 0) return VDIT_E_SHAPE;
     uint64_t n_tok = 1;
     if (!mul_ok(n_tok, T) || !mul_ok(n_tok, Hp) || !mul_ok(n_tok, Wp)) return VDIT_E_SHAPE;
@@ -54,12 +69,31 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
     // whose byte range is a signed 32-bit value.
     if (dt == VDIT_BF16 && n_tok * (uint64_t)heads * (uint64_t)D * 2u >= (uint64_t(1) << 31)) return VDIT_E_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return VDIT_E_ALIGN;
+    if (rope && !split_ok(D, rope->split[0], rope->split[1], rope->split[2])) return VDIT_E_ROPE_SPLIT;
+    if (rope && (!(rope->theta > 0.f) || !std::isfinite(rope->theta))) return VDIT_E_SHAPE;
     if (overlap(o, bytes, q, bytes) || overlap(o, bytes, k, bytes) || overlap(o, bytes, v, bytes))
         return VDIT_E_ALIAS;
 
     const float s = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)D));
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int HW = Hp * Wp;
+    if (rope) {
+        FlashRope fr{};
+        fr.T = T;
+        fr.Hp = Hp;
+        fr.Wp = Wp;
+        fr.b1 = rope->split[0] / 2;
+        fr.b2 = (rope->split[0] + rope->split[1]) / 2;
+        int j = 0;
+        for (int a = 0; a < 3; ++a)
+            for (int jj = 0; jj < rope->split[a] / 2; ++jj, ++j)
+                fr.freq_rev[j] = (float)(std::pow((double)rope->theta, -2.0 * jj / (double)rope->split[a]) /
+                                         6.283185307179586476925286766559);
+        const float c = (float)((double)s * kLog2e);
+        if (mode == kFull)
+            return launch_status(launch_flash_rope_bf16(q, k, v, o, B, T * HW, T * HW, heads, D, c, 0, fr, st));
+        return launch_status(launch_flash_rope_bf16(q, k, v, o, B * T, HW, HW, heads, D, c, 1, fr, st));
+    }
     if (dt == VDIT_F32)
         return launch_status(launch_attn_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, B,
                                              heads, T, HW, D, (int)mode, s, st));
@@ -98,6 +132,20 @@ vdit_status_t vdit_attn_full(const void *q, const void *k, const void *v, void *
 vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
                                 int Hp, int Wp, int head_dim, float scale, vdit_dtype_t dtype, void *stream) {
     return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kSpatial);
+}
+
+vdit_status_t vdit_attn_full_rope(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
+                                  int Hp, int Wp, int head_dim, int d_t, int d_h, int d_w, float theta, float scale,
+                                  vdit_dtype_t dtype, void *stream) {
+    const AttnRope r{{d_t, d_h, d_w}, theta};
+    return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kFull, &r);
+}
+
+vdit_status_t vdit_attn_spatial_rope(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
+                                     int Hp, int Wp, int head_dim, int d_t, int d_h, int d_w, float theta,
+                                     float scale, vdit_dtype_t dtype, void *stream) {
+    const AttnRope r{{d_t, d_h, d_w}, theta};
+    return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kSpatial, &r);
 }
 
 vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
@@ -179,9 +227,7 @@ vdit_status_t vdit_qkv_proj(const void *x, const void *w, const void *bias, cons
     if (dtype == VDIT_BF16 && D != 128) return VDIT_E_HEAD_DIM;
     if (dtype == VDIT_F32 && (D > 256 || D % 2)) return VDIT_E_HEAD_DIM;
     const bool rope_on = d_t != 0 || d_h != 0 || d_w != 0;
-    if (rope_on && (d_t < 0 || d_h < 0 || d_w < 0 || (d_t & 1) || (d_h & 1) || (d_w & 1) ||
-                    (int64_t)d_t + d_h + d_w != D))
-        return VDIT_E_ROPE_SPLIT;
+    if (rope_on && !split_ok(D, d_t, d_h, d_w)) return VDIT_E_ROPE_SPLIT;
     if (rope_on && (!(theta > 0.f) || !std::isfinite(theta))) return VDIT_E_SHAPE;
     if (!(eps >= 0.f) || !std::isfinite(eps)) return VDIT_E_SHAPE;
     uint64_t n_tok = 1, dim = 1;
@@ -279,9 +325,7 @@ vdit_status_t vdit_rope3d(const void *x, void *y, int B, int heads, int T, int H
     if (dtype != VDIT_BF16 && dtype != VDIT_F32) return VDIT_E_DTYPE;
     if (B <= 0 || heads <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || head_dim <= 0) return VDIT_E_SHAPE;
     if (head_dim % 8 || head_dim > 256) return VDIT_E_HEAD_DIM;
-    if (d_t < 0 || d_h < 0 || d_w < 0 || (d_t & 1) || (d_h & 1) || (d_w & 1) ||
-        (int64_t)d_t + d_h + d_w != head_dim)
-        return VDIT_E_ROPE_SPLIT;
+    if (!split_ok(head_dim, d_t, d_h, d_w)) return VDIT_E_ROPE_SPLIT;
     if (!(theta > 0.f) || !std::isfinite(theta)) return VDIT_E_SHAPE;
     uint64_t elems = 1;
     if (!mul_ok(elems, B) || !mul_ok(elems, T) || !mul_ok(elems, Hp) || !mul_ok(elems, Wp) || !mul_ok(elems, heads) ||

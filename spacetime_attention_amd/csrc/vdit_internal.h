@@ -51,6 +51,21 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
                              int L, int Lk, int heads, int D, float scale_log2e, int pass,
                              hipStream_t s);
 
+// 3D RoPE applied inside the flash kernel: to the queries once, and to each
+// K tile as it lands in LDS. Token n of a clip sits at grid position
+// (n / (Hp*Wp), (n / Wp) % Hp, n % Wp) of a T x Hp x Wp grid; pair j
+// (< D/2) turns with t below b1, with h below b2 and with w above, at
+// freq_rev[j] = theta^(-2jj/d_a) / (2 pi) revolutions per grid step.
+struct FlashRope {
+    int T, Hp, Wp, b1, b2;
+    float freq_rev[64];
+};
+// As launch_flash_bf16 for pass 0 (full) or 1 (spatial), with q and k
+// rotated by `rope` on the fly (q and k in memory stay unrotated).
+hipError_t launch_flash_rope_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
+                                  int heads, int D, float scale_log2e, int pass, const FlashRope &rope,
+                                  hipStream_t s);
+
 // Non-overlapping spacetime windows over a (T, Hp, Wp) token grid: window
 // (iwt, iwh, iww) holds tokens t in [iwt*wt, min((iwt+1)*wt, T)) and likewise
 // for h and w; its queries attend to exactly its tokens. wt/wh/ww are clipped

@@ -69,6 +69,32 @@ def test_attention_argument_errors(lib, fn):
         assert call(T=65) == 2
 
 
+@pytest.mark.parametrize("fn", ["vdit_attn_full_rope", "vdit_attn_spatial_rope"])
+def test_attention_rope_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    ok = dict(q=Q, k=K, v=V, o=O, B=1, heads=2, T=3, Hp=4, Wp=5, D=128, split=(44, 42, 42), theta=10000.0,
+              scale=0.0, dt=vd.BF16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["B"], a["heads"], a["T"], a["Hp"], a["Wp"], a["D"],
+                 *a["split"], a["theta"], a["scale"], a["dt"], None)
+
+    assert call(q=None) == 1                      # VDIT_E_NULL
+    assert call(B=0) == 2                         # VDIT_E_SHAPE
+    assert call(T=64, Hp=256, Wp=256, heads=16) == 2
+    assert call(D=96) == 3                        # VDIT_E_HEAD_DIM
+    assert call(dt=vd.F32) == 7                   # bf16 only
+    assert call(dt=7) == 7
+    assert call(split=(44, 42, 40)) == 4          # VDIT_E_ROPE_SPLIT: parts do not sum to D
+    assert call(split=(43, 43, 42)) == 4          # odd part
+    assert call(D=64, split=(44, 42, 42)) == 4
+    assert call(theta=0.0) == 2
+    assert call(theta=float("inf")) == 2
+    assert call(q=Q + 8) == 5                     # VDIT_E_ALIGN
+    assert call(o=K + 16) == 6                    # VDIT_E_ALIAS
+
+
 def test_rope_argument_errors(lib):
     f = lib.vdit_rope3d
 

@@ -271,6 +271,78 @@ def test_720p_full_sampled():
     _sampled_attention("720p_full", "full", 4099)
 
 
+# ----------------------------------------------------------------------------
+# RoPE applied inside the attention kernel
+# ----------------------------------------------------------------------------
+
+ROPE_PASSES = {"full": vd.attn_full_rope, "spatial": vd.attn_spatial_rope}
+ROPE_SMALL = [
+    # (name, B, grid, heads, D, split)
+    # 750 tokens: ragged last key tile and query block.
+    ("rope_ragged_750", 1, (3, 10, 25), 2, 128, (44, 42, 42)),
+    # two clips: the second clip's rows start at token row N, spatial
+    # segments at every frame of both clips.
+    ("rope_two_clips_620", 2, (5, 4, 31), 2, 128, (44, 42, 42)),
+    # 35-token frames: one 64-key tile spans two frame boundaries, so the
+    # per-tile step of the key positions carries into t and h.
+    ("rope_small_frames_140", 2, (4, 5, 7), 2, 128, (44, 42, 42)),
+    # a single row per frame: the w index is always 0 and t steps by 64 / Wp.
+    ("rope_one_row_frames", 1, (30, 1, 9), 2, 128, (44, 42, 42)),
+    ("rope_d64", 1, (5, 6, 9), 3, 64, (24, 20, 20)),
+    ("rope_uneven_split", 1, (3, 7, 11), 2, 128, (64, 32, 32)),
+    ("rope_no_time_part", 1, (3, 7, 11), 2, 128, (0, 64, 64)),
+]
+
+
+def _rope_ref(d, grid, split, mode, rows=None):
+    qr = oracle.rope3d(d["q"].f32, grid, split)
+    kr = oracle.rope3d(d["k"].f32, grid, split)
+    return oracle.attention(qr, kr, d["v"].f32, grid, mode, rows=rows)
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial"])
+@pytest.mark.parametrize("case", ROPE_SMALL, ids=[c[0] for c in ROPE_SMALL])
+def test_attn_rope_small(case, mode):
+    """attention(RoPE(q), RoPE(k), v) with the rotation inside the kernel,
+    against the oracle's RoPE followed by its attention."""
+    name, B, grid, heads, D, split = case
+    _announce(f"attn {mode} with fused RoPE {name} B={B} grid={grid} heads={heads} D={D} split={split}")
+    w = small_grid(name, B, *grid, heads, D, "bf16", seed=200 + len(name))
+    d, (q, k, v) = _qkv(w)
+    q0, k0 = q.clone(), k.clone()
+    got = to_host(ROPE_PASSES[mode](q, k, v, grid, split))
+    torch.cuda.synchronize()
+    assert_close(got, _rope_ref(d, grid, split, mode), "bf16", f"{name}/{mode}+rope")
+    # q and k in memory are left unrotated.
+    assert torch.equal(q.view(torch.int16), q0.view(torch.int16))
+    assert torch.equal(k.view(torch.int16), k0.view(torch.int16))
+
+
+def test_attn_rope_theta_and_scale():
+    """Another base and an explicit softmax scale reach the kernel."""
+    grid, split = (3, 10, 25), (44, 42, 42)
+    _announce("attn full with fused RoPE, theta 500, scale 0.05")
+    w = small_grid("rope_theta", 1, *grid, 2, 128, "bf16", seed=233)
+    d, (q, k, v) = _qkv(w)
+    got = to_host(vd.attn_full_rope(q, k, v, grid, split, theta=500.0, scale=0.05))
+    qr = oracle.rope3d(d["q"].f32, grid, split, theta=500.0)
+    kr = oracle.rope3d(d["k"].f32, grid, split, theta=500.0)
+    ref = oracle.attention(qr, kr, d["v"].f32, grid, "full", scale=0.05)
+    assert_close(got, ref, "bf16", "full+rope/theta500")
+
+
+@pytest.mark.parametrize("wname,mode,stride", [("480p_full", "full", 512), ("480p_divided", "spatial", 97)])
+def test_480p_attn_rope_sampled(wname, mode, stride):
+    w = WORKLOADS[wname]
+    grid, split = (w.T, w.Hp, w.Wp), (44, 42, 42)
+    _announce(f"{wname} {mode} with fused RoPE, full size, rows every {stride}")
+    d, (q, k, v) = _qkv(w)
+    got = ROPE_PASSES[mode](q, k, v, grid, split)
+    rows = sample_rows(w.N, stride, offset=stride // 5)
+    got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
+    assert_close(got_rows, _rope_ref(d, grid, split, mode, rows=rows), "bf16", f"{wname}/{mode}+rope")
+
+
 def test_block_input_path():
     """Latent (1,16,21,60,104) -> patchify -> RoPE -> spatial -> temporal."""
     w = WORKLOADS["block_input"]
