@@ -227,7 +227,8 @@ def main():
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch),
                            "rope_in_attention": bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_,
-                                                                        os_, grid, f_full, f_spatial)}
+                                                                        os_, ot, grid, f_full, f_spatial,
+                                                                        b_temporal)}
     if not args.no_720p:
         result["full_720p"] = bench_full_720p(vd, torch)
     if not args.no_mfma_probe:
@@ -362,13 +363,14 @@ def bench_window(vd, torch, iters: int = 20):
             "ms": ms, "tflops": flop / ms / 1e9, "frac_bf16_peak": flop / ms / 1e9 / PEAK_BF16_TFLOPS}
 
 
-def bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_, od, grid, f_full, f_spatial,
+def bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_, od, ot, grid, f_full, f_spatial, b_temporal,
                             rounds: int = 3, iters: int = 10):
     """RoPE applied inside the attention kernel against the separate RoPE
     pass on Q and on K followed by the plain kernel, on the step's full
-    (batch 1) and spatial (batch 2) inputs, timed on their own after the
+    (batch 1) and divided (batch 2) inputs, timed on their own after the
     step in alternating blocks of `iters` launches so that both see the same
-    clock. The FLOP rates count only the attention product."""
+    clock. The FLOP rates count only the attention product; the temporal
+    rate is its algorithmic bytes (Q, K, V read and O written once)."""
     split = (44, 42, 42)
 
     def sep(q, k, v, o, attn):
@@ -383,7 +385,8 @@ def bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_, od, grid, f_
     out = {}
     for name, q, k, v, o, plain, fused, flop in (
             ("full", qf, kf, vf, of, vd.attn_full, vd.attn_full_rope, f_full),
-            ("spatial", qd, kd, vd_, od, vd.attn_spatial, vd.attn_spatial_rope, f_spatial)):
+            ("spatial", qd, kd, vd_, od, vd.attn_spatial, vd.attn_spatial_rope, f_spatial),
+            ("temporal", qd, kd, vd_, ot, vd.attn_temporal, vd.attn_temporal_rope, None)):
         runs = {"fused": lambda: fused(q, k, v, grid, split, out=o), "separate": sep(q, k, v, o, plain)}
         ms = {key: [] for key in runs}
         for key, fn in runs.items():
@@ -399,11 +402,15 @@ def bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_, od, grid, f_
                 ms[key].append(a.elapsed_time(b) / iters)
         med = {key: float(np.median(v_)) for key, v_ in ms.items()}
         out[name] = {"fused_ms": med["fused"], "separate_ms": med["separate"],
-                     "fused_tflops": flop / med["fused"] / 1e9,
                      "fused_over_separate": med["fused"] / med["separate"]}
+        if flop is not None:
+            out[name]["fused_tflops"] = flop / med["fused"] / 1e9
+        else:
+            out[name]["fused_gbs"] = b_temporal / med["fused"] / 1e6
         del runs
     out["workload"] = f"480p grid {grid}, 12 heads x 128, split {split}: full [1,32760,12,128], " \
-                      f"spatial [2,32760,12,128]; separate = vdit_rope3d on q and on k, then the plain pass"
+                      f"spatial and temporal [2,32760,12,128]; separate = vdit_rope3d on q and on k, " \
+                      f"then the plain pass"
     return out
 
 

@@ -10,9 +10,10 @@
  *   vdit_attn_full      softmax attention over all T*Hp*Wp tokens of a clip;
  *   vdit_attn_spatial   the same, with keys limited to the query's own latent
  *                       frame;
- *   vdit_attn_full_rope, vdit_attn_spatial_rope
- *                       the two above with 3D RoPE applied to q and k inside
- *                       the attention kernel (no separate RoPE pass);
+ *   vdit_attn_full_rope, vdit_attn_spatial_rope, vdit_attn_temporal_rope
+ *                       full, spatial and temporal attention with 3D RoPE
+ *                       applied to q and k inside the attention kernel (no
+ *                       separate RoPE pass);
  *   vdit_attn_temporal  the same, with keys limited to the query's own patch
  *                       position across frames;
  *   vdit_attn_cross     attention from the video tokens to another token set
@@ -167,15 +168,18 @@ vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, voi
                                 float scale, vdit_dtype_t dtype, void *stream);
 
 /*
- * vdit_attn_full_rope, vdit_attn_spatial_rope — full or spatial attention of
- * the rotated queries and keys: the result equals vdit_rope3d on q and on k
- * (same d_t, d_h, d_w, theta) followed by vdit_attn_full or
- * vdit_attn_spatial, without the rotated copies ever reaching memory. In Wan
- * 2.1's attn1 ("How AI Generates Video ...", section 5) the rotation is the
- * step right before the attention product; here the kernel applies it to the
+ * vdit_attn_full_rope, vdit_attn_spatial_rope, vdit_attn_temporal_rope —
+ * full, spatial or temporal attention of the rotated queries and keys: the
+ * result equals vdit_rope3d on q and on k (same d_t, d_h, d_w, theta)
+ * followed by vdit_attn_full, vdit_attn_spatial or vdit_attn_temporal,
+ * without the rotated copies ever reaching memory. In Wan 2.1's attn1 ("How
+ * AI Generates Video ...", section 5) the rotation is the step right before
+ * the attention product. The full and spatial kernels apply it to the
  * queries once after reading them and to every K tile as it arrives in
  * on-chip memory, so it is repeated once per query block that reads the
- * tile. q and k in memory are not modified.
+ * tile; the temporal kernel rotates each sequence's Q and K rows once, in
+ * on-chip memory. q and k in memory are not modified. T as
+ * vdit_attn_temporal for the temporal call (<= 64).
  *
  * Arguments, layouts, limits and errors as vdit_attn_full, plus d_t, d_h,
  * d_w and theta as vdit_rope3d (VDIT_E_ROPE_SPLIT for a bad split,
@@ -193,6 +197,10 @@ vdit_status_t vdit_attn_spatial_rope(const void *q, const void *k, const void *v
                                      int B, int heads, int T, int Hp, int Wp, int head_dim,
                                      int d_t, int d_h, int d_w, float theta, float scale,
                                      vdit_dtype_t dtype, void *stream);
+vdit_status_t vdit_attn_temporal_rope(const void *q, const void *k, const void *v, void *o,
+                                      int B, int heads, int T, int Hp, int Wp, int head_dim,
+                                      int d_t, int d_h, int d_w, float theta, float scale,
+                                      vdit_dtype_t dtype, void *stream);
 
 /*
  * vdit_attn_temporal — the temporal pass of divided attention.

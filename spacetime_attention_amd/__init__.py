@@ -15,6 +15,7 @@ Functions (names as in the C ABI, without the ``vdit_`` prefix):
   attn_spatial(q, k, v, grid, scale=0.0, out=None)
   attn_full_rope(q, k, v, grid, split=(44, 42, 42), theta=10000.0, scale=0.0, out=None)
   attn_spatial_rope(q, k, v, grid, split=(44, 42, 42), theta=10000.0, scale=0.0, out=None)
+  attn_temporal_rope(q, k, v, grid, split=(44, 42, 42), theta=10000.0, scale=0.0, out=None)
   attn_temporal(q, k, v, grid, scale=0.0, out=None)
   attn_cross(q, k, v, scale=0.0, out=None)
   attn_window(q, k, v, grid, window, scale=0.0, out=None)
@@ -38,7 +39,8 @@ BF16, F32 = 0, 1
 STATUS = ["VDIT_OK", "VDIT_E_NULL", "VDIT_E_SHAPE", "VDIT_E_HEAD_DIM", "VDIT_E_ROPE_SPLIT",
           "VDIT_E_ALIGN", "VDIT_E_ALIAS", "VDIT_E_DTYPE", "VDIT_E_LAUNCH"]
 EXPORTS = ("vdit_status_str", "vdit_patchify", "vdit_rope3d", "vdit_attn_full",
-           "vdit_attn_spatial", "vdit_attn_full_rope", "vdit_attn_spatial_rope", "vdit_attn_temporal",
+           "vdit_attn_spatial", "vdit_attn_full_rope", "vdit_attn_spatial_rope", "vdit_attn_temporal_rope",
+           "vdit_attn_temporal",
            "vdit_attn_cross", "vdit_attn_window", "vdit_qkv_proj")
 
 
@@ -72,7 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp] + [i] * 6 + [f, i, vp]
         fn.restype = i
-    for name in ("vdit_attn_full_rope", "vdit_attn_spatial_rope"):
+    for name in ("vdit_attn_full_rope", "vdit_attn_spatial_rope", "vdit_attn_temporal_rope"):
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp] + [i] * 9 + [f, f, i, vp]
         fn.restype = i
@@ -219,6 +221,12 @@ def attn_spatial_rope(q, k, v, grid, split: Sequence[int] = (44, 42, 42), theta:
                       scale: float = 0.0, out=None) -> torch.Tensor:
     """Spatial attention of RoPE(q) against RoPE(k), rotated inside the kernel."""
     return _attn_rope("vdit_attn_spatial_rope", q, k, v, grid, split, theta, scale, out)
+
+
+def attn_temporal_rope(q, k, v, grid, split: Sequence[int] = (44, 42, 42), theta: float = 10000.0,
+                       scale: float = 0.0, out=None) -> torch.Tensor:
+    """Temporal attention of RoPE(q) against RoPE(k), rotated inside the kernel."""
+    return _attn_rope("vdit_attn_temporal_rope", q, k, v, grid, split, theta, scale, out)
 
 
 def attn_temporal(q, k, v, grid, scale: float = 0.0, out=None) -> torch.Tensor:

@@ -25,6 +25,11 @@
 //    O^T = V^T P^T with V^T read through ds_read_b64_tr_b16.
 //  * O is staged through the Q slice and written back as whole 16-byte row
 //    chunks.
+//  * The RoPE instantiation rotates the sequence's Q and K rows in the LDS
+//    slice once they have landed: each lane rewrites the 16-byte chunks its
+//    own loads wrote. A Q chunk and the K chunk at the same place belong to
+//    the same frame and feature pairs, so they share their angles; every
+//    row is rotated exactly once, as the separate RoPE pass would.
 #include "vdit_internal.h"
 
 namespace vdit {
@@ -72,10 +77,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 // with -inf and in query columns that are never stored. V always has TP
 // rows, zero past T, because a zero weight times non-finite padding would
 // not be zero.
-template <int D, int KB, int QKR>
+template <int D, int KB, int QKR, bool ROPE>
 __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    uint16_t *__restrict__ o, int B, int heads, int T, int HW, float c)
+    uint16_t *__restrict__ o, int B, int heads, int T, int HW, float c, FlashRope fr)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int TP = 32 * KB;      // padded sequence length
@@ -128,6 +133,35 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     // Loads complete in issue order: with only the TP/RPL V loads still
     // outstanding, this wave's Q and K rows are in its LDS slice.
     wait_vmem_upto<TP / RPL>();
+
+    if constexpr (ROPE) {
+        // Row r of the slices is frame r at patch position p = (h, w). Pair j
+        // turns with t below b1, with h below b2 and with w above; the angle
+        // is taken in revolutions, reduced to [0, 1) for v_sin/v_cos.
+        const float fh = (float)(int)(p / fr.Wp), fw = (float)(int)(p % fr.Wp);
+#pragma unroll
+        for (int i = 0; i < QKR / RPL; ++i) {
+            const int r = RPL * i + lane / CH;
+            const int lc = (lane % CH) ^ swz_k<D>(r, 0);
+            auto *qp = (__attribute__((address_space(3))) u32x4 *)(qs_ + i * 1024 + 16 * lane);
+            auto *kp = (__attribute__((address_space(3))) u32x4 *)(ks_ + i * 1024 + 16 * lane);
+            u32x4 xq = *qp, xk = *kp;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * lc + e;
+                const float pos = j < fr.b1 ? (float)r : (j < fr.b2 ? fh : fw);
+                const float rev = __builtin_amdgcn_fractf(pos * fr.freq_rev[j]);
+                const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                float x0 = __uint_as_float(xq[e] << 16), x1 = __uint_as_float(xq[e] & 0xffff0000u);
+                xq[e] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+                x0 = __uint_as_float(xk[e] << 16);
+                x1 = __uint_as_float(xk[e] & 0xffff0000u);
+                xk[e] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+            }
+            *qp = xq;
+            *kp = xk;
+        }
+    }
 
     // S^T = K Q^T: K rows as A operands, Q rows as B operands.
     f32x16 sacc[KB][KB];
@@ -246,31 +280,42 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
 #endif
 }
 
-template <int D, int KB, int QKR>
+template <int D, int KB, int QKR, bool ROPE>
 hipError_t launch(const void *q, const void *k, const void *v, void *o, int B, int heads, int T, int HW,
-                  float c, hipStream_t s) {
+                  float c, hipStream_t s, const FlashRope &fr) {
     const int64_t total = (int64_t)B * HW * heads;
     const uint32_t grid = (uint32_t)((total + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((temporal_bf16<D, KB, QKR>), dim3(grid), dim3(kWaves * 64), 0, s, (const uint16_t *)q,
-                       (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, B, heads, T, HW, c);
+    hipLaunchKernelGGL((temporal_bf16<D, KB, QKR, ROPE>), dim3(grid), dim3(kWaves * 64), 0, s, (const uint16_t *)q,
+                       (const uint16_t *)k, (const uint16_t *)v, (uint16_t *)o, B, heads, T, HW, c, fr);
     return hipGetLastError();
+}
+
+template <bool ROPE>
+hipError_t dispatch(const void *q, const void *k, const void *v, void *o, int B, int heads, int T, int HW, int D,
+                    float c, hipStream_t s, const FlashRope &fr) {
+    if (T <= 24) {
+        if (D == 128) return launch<128, 1, 24, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        if (D == 64) return launch<64, 1, 24, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+    } else if (T <= 32) {
+        if (D == 128) return launch<128, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        if (D == 64) return launch<64, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+    } else if (T <= 64) {
+        if (D == 128) return launch<128, 2, 64, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        if (D == 64) return launch<64, 2, 64, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_temporal_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
                                 int HW, int D, float scale_log2e, hipStream_t s) {
-    if (T <= 24) {
-        if (D == 128) return launch<128, 1, 24>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-        if (D == 64) return launch<64, 1, 24>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-    } else if (T <= 32) {
-        if (D == 128) return launch<128, 1, 32>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-        if (D == 64) return launch<64, 1, 32>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-    } else if (T <= 64) {
-        if (D == 128) return launch<128, 2, 64>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-        if (D == 64) return launch<64, 2, 64>(q, k, v, o, B, heads, T, HW, scale_log2e, s);
-    }
-    return hipErrorInvalidValue;
+    return dispatch<false>(q, k, v, o, B, heads, T, HW, D, scale_log2e, s, FlashRope{});
+}
+
+hipError_t launch_temporal_rope_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
+                                     int HW, int D, float scale_log2e, const FlashRope &rope, hipStream_t s) {
+    return dispatch<true>(q, k, v, o, B, heads, T, HW, D, scale_log2e, s, rope);
 }
 
 }  // namespace vdit

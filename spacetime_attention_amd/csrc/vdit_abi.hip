@@ -92,7 +92,9 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
         const float c = (float)((double)s * kLog2e);
         if (mode == kFull)
             return launch_status(launch_flash_rope_bf16(q, k, v, o, B, T * HW, T * HW, heads, D, c, 0, fr, st));
-        return launch_status(launch_flash_rope_bf16(q, k, v, o, B * T, HW, HW, heads, D, c, 1, fr, st));
+        if (mode == kSpatial)
+            return launch_status(launch_flash_rope_bf16(q, k, v, o, B * T, HW, HW, heads, D, c, 1, fr, st));
+        return launch_status(launch_temporal_rope_bf16(q, k, v, o, B, heads, T, HW, D, c, fr, st));
     }
     if (dt == VDIT_F32)
         return launch_status(launch_attn_f32((const float *)q, (const float *)k, (const float *)v, (float *)o, B,
@@ -146,6 +148,13 @@ vdit_status_t vdit_attn_spatial_rope(const void *q, const void *k, const void *v
                                      float scale, vdit_dtype_t dtype, void *stream) {
     const AttnRope r{{d_t, d_h, d_w}, theta};
     return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kSpatial, &r);
+}
+
+vdit_status_t vdit_attn_temporal_rope(const void *q, const void *k, const void *v, void *o, int B, int heads,
+                                      int T, int Hp, int Wp, int head_dim, int d_t, int d_h, int d_w, float theta,
+                                      float scale, vdit_dtype_t dtype, void *stream) {
+    const AttnRope r{{d_t, d_h, d_w}, theta};
+    return attn(q, k, v, o, B, heads, T, Hp, Wp, head_dim, scale, dtype, stream, kTemporal, &r);
 }
 
 vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,

@@ -51,8 +51,9 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
                              int L, int Lk, int heads, int D, float scale_log2e, int pass,
                              hipStream_t s);
 
-// 3D RoPE applied inside the flash kernel: to the queries once, and to each
-// K tile as it lands in LDS. Token n of a clip sits at grid position
+// 3D RoPE applied inside an attention kernel (the flash kernel: to the
+// queries once, and to each K tile as it lands in LDS; the temporal kernel:
+// to each sequence's Q and K rows in LDS). Token n of a clip sits at grid position
 // (n / (Hp*Wp), (n / Wp) % Hp, n % Wp) of a T x Hp x Wp grid; pair j
 // (< D/2) turns with t below b1, with h below b2 and with w above, at
 // freq_rev[j] = theta^(-2jj/d_a) / (2 pi) revolutions per grid step.
@@ -94,6 +95,11 @@ hipError_t launch_cross_f32(const float *q, const float *k, const float *v, floa
 // tokens at stride HW tokens.
 hipError_t launch_temporal_bf16(const void *q, const void *k, const void *v, void *o, int B,
                                 int heads, int T, int HW, int D, float scale_log2e, hipStream_t s);
+
+// The temporal pass with q and k rotated by `rope` (FlashRope, above) in
+// on-chip memory; q and k in memory stay unrotated.
+hipError_t launch_temporal_rope_bf16(const void *q, const void *k, const void *v, void *o, int B, int heads, int T,
+                                     int HW, int D, float scale_log2e, const FlashRope &rope, hipStream_t s);
 
 // Patchify as an implicit-im2col GEMM.
 struct PatchGeom {

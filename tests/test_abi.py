@@ -69,7 +69,7 @@ def test_attention_argument_errors(lib, fn):
         assert call(T=65) == 2
 
 
-@pytest.mark.parametrize("fn", ["vdit_attn_full_rope", "vdit_attn_spatial_rope"])
+@pytest.mark.parametrize("fn", ["vdit_attn_full_rope", "vdit_attn_spatial_rope", "vdit_attn_temporal_rope"])
 def test_attention_rope_argument_errors(lib, fn):
     f = getattr(lib, fn)
     ok = dict(q=Q, k=K, v=V, o=O, B=1, heads=2, T=3, Hp=4, Wp=5, D=128, split=(44, 42, 42), theta=10000.0,
@@ -93,6 +93,8 @@ def test_attention_rope_argument_errors(lib, fn):
     assert call(theta=float("inf")) == 2
     assert call(q=Q + 8) == 5                     # VDIT_E_ALIGN
     assert call(o=K + 16) == 6                    # VDIT_E_ALIAS
+    if fn == "vdit_attn_temporal_rope":
+        assert call(T=65) == 2
 
 
 def test_rope_argument_errors(lib):

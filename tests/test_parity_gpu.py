@@ -275,7 +275,7 @@ def test_720p_full_sampled():
 # RoPE applied inside the attention kernel
 # ----------------------------------------------------------------------------
 
-ROPE_PASSES = {"full": vd.attn_full_rope, "spatial": vd.attn_spatial_rope}
+ROPE_PASSES = {"full": vd.attn_full_rope, "spatial": vd.attn_spatial_rope, "temporal": vd.attn_temporal_rope}
 ROPE_SMALL = [
     # (name, B, grid, heads, D, split)
     # 750 tokens: ragged last key tile and query block.
@@ -288,6 +288,8 @@ ROPE_SMALL = [
     ("rope_small_frames_140", 2, (4, 5, 7), 2, 128, (44, 42, 42)),
     # a single row per frame: the w index is always 0 and t steps by 64 / Wp.
     ("rope_one_row_frames", 1, (30, 1, 9), 2, 128, (44, 42, 42)),
+    # 40 frames: the temporal kernel's two-block form (T > 32).
+    ("rope_long_time_40", 1, (40, 2, 3), 2, 128, (44, 42, 42)),
     ("rope_d64", 1, (5, 6, 9), 3, 64, (24, 20, 20)),
     ("rope_uneven_split", 1, (3, 7, 11), 2, 128, (64, 32, 32)),
     ("rope_no_time_part", 1, (3, 7, 11), 2, 128, (0, 64, 64)),
@@ -300,7 +302,7 @@ def _rope_ref(d, grid, split, mode, rows=None):
     return oracle.attention(qr, kr, d["v"].f32, grid, mode, rows=rows)
 
 
-@pytest.mark.parametrize("mode", ["full", "spatial"])
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
 @pytest.mark.parametrize("case", ROPE_SMALL, ids=[c[0] for c in ROPE_SMALL])
 def test_attn_rope_small(case, mode):
     """attention(RoPE(q), RoPE(k), v) with the rotation inside the kernel,
@@ -318,7 +320,7 @@ def test_attn_rope_small(case, mode):
     assert torch.equal(k.view(torch.int16), k0.view(torch.int16))
 
 
-@pytest.mark.parametrize("mode", ["full", "spatial"])
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
 def test_attn_rope_peaky(mode):
     """Q and K of standard deviation 4 (logits of standard deviation 16):
     the running maximum is raised often, on rotated operands. The kernel
@@ -350,7 +352,8 @@ def test_attn_rope_theta_and_scale():
     assert_close(got, ref, "bf16", "full+rope/theta500")
 
 
-@pytest.mark.parametrize("wname,mode,stride", [("480p_full", "full", 512), ("480p_divided", "spatial", 97)])
+@pytest.mark.parametrize("wname,mode,stride", [("480p_full", "full", 512), ("480p_divided", "spatial", 97),
+                                               ("480p_divided", "temporal", 89)])
 def test_480p_attn_rope_sampled(wname, mode, stride):
     w = WORKLOADS[wname]
     grid, split = (w.T, w.Hp, w.Wp), (44, 42, 42)
