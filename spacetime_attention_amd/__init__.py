@@ -301,10 +301,18 @@ def qkv_proj(x, w, bias=None, gamma_q=None, gamma_k=None, *, grid, heads: int, h
 def divided(x: torch.Tensor, grid, order=("spatial", "temporal"), split: Optional[Sequence[int]] = None,
             theta: float = 10000.0) -> torch.Tensor:
     """A chain of passes over tokens ``x [B, N, heads, D]``: each pass takes
-    q = k = RoPE(x) (or x when ``split`` is None) and v = x."""
+    q = k = RoPE(x) (or x when ``split`` is None) and v = x.
+
+    With a split, a bf16 temporal pass runs the kernel that rotates q and k
+    itself (faster than a separate RoPE pass there, as that pass is bound
+    by memory traffic); the full and spatial passes keep the separate RoPE
+    pass, which is faster for them."""
     fns = {"spatial": attn_spatial, "temporal": attn_temporal, "full": attn_full}
     cur = x
     for mode in order:
+        if split is not None and mode == "temporal" and cur.dtype == torch.bfloat16:
+            cur = attn_temporal_rope(cur, cur, cur, grid, split, theta)
+            continue
         qk = rope3d(cur, grid, split, theta) if split is not None else cur
         cur = fns[mode](qk, qk, cur, grid)
     return cur

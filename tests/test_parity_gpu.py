@@ -339,6 +339,22 @@ def test_attn_rope_peaky(mode):
     assert_close(got, ref, "bf16", f"peaky/{mode}+rope")
 
 
+@pytest.mark.parametrize("order", [("spatial", "temporal"), ("temporal", "spatial")])
+def test_divided_chain_with_rope_bf16(order):
+    """The binding's divided() chain with RoPE in bf16 (its temporal pass
+    rotates inside the kernel, its spatial pass after a separate RoPE
+    pass) against the oracle's chain with every stored intermediate, the
+    rotated q/k included, rounded to bf16."""
+    grid, split = (5, 6, 9), (44, 42, 42)
+    _announce(f"divided chain {order} with RoPE, bf16, grid={grid}")
+    w = small_grid("divided_rope", 1, *grid, 2, 128, "bf16", seed=41)
+    d = w.draw_qkv()
+    x = to_dev(d["q"])
+    got = to_host(vd.divided(x, grid, order=order, split=split))
+    ref = oracle.divided(d["q"].f32, grid, order, rope_split=split, storage="bf16")
+    assert_close(got, ref, "bf16", f"divided/{'-'.join(order)}+rope")
+
+
 def test_attn_rope_theta_and_scale():
     """Another base and an explicit softmax scale reach the kernel."""
     grid, split = (3, 10, 25), (44, 42, 42)
