@@ -115,6 +115,21 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc((void *)(q + base), 0, nrec, kBufferFlags);
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void *)(k + base), 0, nrec, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void *)(v + base), 0, nrec, kBufferFlags);
+    // RoPE: the frequencies of the four pairs in each chunk this lane loads,
+    // read from the kernel arguments before any tile load is issued. Loads
+    // complete in issue order, so reading them after the V loads would make
+    // the rotation wait for all of V.
+    f32x4 fq[ROPE ? QKR / RPL : 1];
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int i = 0; i < QKR / RPL; ++i) {
+            const int r = RPL * i + lane / CH;
+            const int lc = (lane % CH) ^ swz_k<D>(r, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fq[i][e] = fr.freq_rev[4 * lc + e];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // Q and K first, V last: the score products only wait for Q and K, and
     // V's loads keep streaming under them.
 #pragma unroll
@@ -150,7 +165,7 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * lc + e;
                 const float pos = j < fr.b1 ? (float)r : (j < fr.b2 ? fh : fw);
-                const float rev = __builtin_amdgcn_fractf(pos * fr.freq_rev[j]);
+                const float rev = __builtin_amdgcn_fractf(pos * fq[i][e]);
                 const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
                 float x0 = __uint_as_float(xq[e] << 16), x1 = __uint_as_float(xq[e] & 0xffff0000u);
                 xq[e] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
