@@ -3,12 +3,18 @@
 TEST INFRASTRUCTURE (part of the oracle): used by the tests and by the
 benchmark for its algorithmic FLOP and byte counts' cross-checks only.
 
-Each function is the plain formula of the passage it cites.
+Each function states, in its own terms, the rule of the passage it cites.
 """
 
 from __future__ import annotations
 
-from typing import Tuple
+from typing import Sequence, Tuple
+
+# Wan2.1's causal VAE compresses time by 4 and each spatial axis by 8
+# ("Video Diffusion Models, in depth", Step 1); its DiT cuts the latent
+# into bricks of 1 latent frame by 2 x 2 latent pixels (same page, Step 2).
+WAN_COMPRESSION = (4, 8, 8)
+WAN_PATCH = (1, 2, 2)
 
 
 def count_tokens(T: int, H: int, W: int, p_t: int = 2, p_h: int = 8, p_w: int = 8) -> int:
@@ -19,10 +25,11 @@ def count_tokens(T: int, H: int, W: int, p_t: int = 2, p_h: int = 8, p_w: int = 
 
 
 def latent_frames(frames: int, t_stride: int = 4) -> int:
-    """Causal VAE frame rule: the first frame alone, then every t_stride frames
-    make one latent frame ("Video Diffusion Models, in depth", Step 1 and the
-    video_tokens function of Step 2)."""
-    return 1 + (frames - 1) // t_stride
+    """Causal VAE frame rule: frame 0 becomes a latent frame of its own and
+    every further run of t_stride frames becomes one more ("Video Diffusion
+    Models, in depth", Step 1: 81 frames give 1 + 80/4 = 21)."""
+    rest = frames - 1
+    return 1 + rest // t_stride
 
 
 def latent_frames_ceil(frames: int, t_comp: int = 4) -> int:
@@ -30,28 +37,38 @@ def latent_frames_ceil(frames: int, t_comp: int = 4) -> int:
     return -(-frames // t_comp)
 
 
-def token_grid(frames: int, height: int, width: int, vae_stride=(4, 8, 8),
-               patch=(1, 2, 2)) -> Tuple[int, int, int]:
-    """(T, Hp, Wp) after the causal VAE and the patch ("Video Diffusion Models,
-    in depth", Step 2, video_tokens)."""
-    t_lat = latent_frames(frames, vae_stride[0])
-    h_lat, w_lat = height // vae_stride[1], width // vae_stride[2]
-    return (t_lat // patch[0], h_lat // patch[1], w_lat // patch[2])
+def spacetime_grid(frames: int, height: int, width: int,
+                   compression: Sequence[int] = WAN_COMPRESSION,
+                   patch: Sequence[int] = WAN_PATCH) -> Tuple[int, int, int]:
+    """Token grid (T, Hp, Wp) of a clip: the VAE's latent extents (time by
+    the causal rule, each spatial axis divided by its stride), each then
+    divided by the brick along that axis; remainders are dropped ("Video
+    Diffusion Models, in depth", Steps 1 and 2)."""
+    latent = (latent_frames(frames, compression[0]),
+              height // compression[1],
+              width // compression[2])
+    return tuple(extent // brick for extent, brick in zip(latent, patch))
 
 
-def video_tokens(frames: int, height: int, width: int, vae_stride=(4, 8, 8),
-                 patch=(1, 2, 2)) -> int:
-    T, Hp, Wp = token_grid(frames, height, width, vae_stride, patch)
+def spacetime_tokens(frames: int, height: int, width: int,
+                     compression: Sequence[int] = WAN_COMPRESSION,
+                     patch: Sequence[int] = WAN_PATCH) -> int:
+    """Number of spacetime tokens: the product of the grid's extents."""
+    T, Hp, Wp = spacetime_grid(frames, height, width, compression, patch)
     return T * Hp * Wp
 
 
-def forward_flops(tokens: int, params: float = 14e9, layers: int = 40,
-                  dim: int = 5120) -> Tuple[float, float]:
-    """Dense FLOPs 2*params*N and attention FLOPs 4*N^2*dim*layers
-    ("Video Diffusion Models, in depth", Step 2, forward_flops)."""
-    dense = 2 * params * tokens
-    attn = 4 * tokens * tokens * dim * layers
-    return dense, attn
+def dense_flop(params: float, tokens: int) -> float:
+    """Every weight takes part in one multiply-add per token: 2*P*N FLOP per
+    forward ("Video Diffusion Models, in depth", Step 2)."""
+    return 2.0 * params * tokens
+
+
+def attention_flop(tokens: int, width: int, layers: int) -> float:
+    """The score product and the value product, over every layer: 4*N^2*dim
+    FLOP per forward ("Video Diffusion Models, in depth", Step 2)."""
+    per_layer = 2 * (2 * tokens * tokens * width)  # two N x N x width products, 2 FLOP per multiply-add
+    return float(per_layer * layers)
 
 
 def attention_flops_full(B: int, heads: int, N: int, D: int) -> int:

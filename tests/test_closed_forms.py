@@ -20,12 +20,12 @@ def _tuple(page_values, key):
 
 
 def test_token_counts(page_values):
-    assert cf.video_tokens(81, 480, 832) == _int(page_values, "tokens_81f_480p")
-    assert cf.video_tokens(81, 720, 1280) == _int(page_values, "tokens_81f_720p")
-    assert cf.video_tokens(17, 480, 832) == _int(page_values, "tokens_17f_480p")
-    assert cf.token_grid(81, 480, 832) == _tuple(page_values, "grid_81f_480p")
-    assert cf.token_grid(17, 480, 832) == _tuple(page_values, "grid_17f_480p")
-    T, Hp, Wp = cf.token_grid(81, 480, 832)
+    assert cf.spacetime_tokens(81, 480, 832) == _int(page_values, "tokens_81f_480p")
+    assert cf.spacetime_tokens(81, 720, 1280) == _int(page_values, "tokens_81f_720p")
+    assert cf.spacetime_tokens(17, 480, 832) == _int(page_values, "tokens_17f_480p")
+    assert cf.spacetime_grid(81, 480, 832) == _tuple(page_values, "grid_81f_480p")
+    assert cf.spacetime_grid(17, 480, 832) == _tuple(page_values, "grid_17f_480p")
+    T, Hp, Wp = cf.spacetime_grid(81, 480, 832)
     assert Hp * Wp == _int(page_values, "tokens_per_slice_480p")
 
 
@@ -65,9 +65,9 @@ def test_pair_counts(page_values):
     npix = _int(page_values, "raw_pixels_81f")
     assert cf.full_pairs(npix) == _int(page_values, "raw_pairs_81f")
     assert cf.fp16_bytes(cf.full_pairs(npix)) == _int(page_values, "raw_fp16_bytes_81f")
-    n = cf.video_tokens(81, 480, 832)
+    n = cf.spacetime_tokens(81, 480, 832)
     assert cf.full_pairs(n) == _int(page_values, "token_pairs_81f")
-    assert cf.full_pairs(cf.video_tokens(17, 480, 832)) == _int(page_values, "token_pairs_17f")
+    assert cf.full_pairs(cf.spacetime_tokens(17, 480, 832)) == _int(page_values, "token_pairs_17f")
     ratio = cf.full_pairs(npix) / cf.full_pairs(n)
     assert round(ratio, 1) == float(page_values["pair_reduction"][0])
     assert round(cf.fp16_bytes(cf.full_pairs(n)) / 1e9, 2) == float(page_values["token_fp16_gb"][0])
@@ -75,8 +75,10 @@ def test_pair_counts(page_values):
 
 @pytest.mark.parametrize("res,h,w", [("480p", 480, 832), ("720p", 720, 1280)])
 def test_forward_flops_prints(page_values, res, h, w):
-    n = cf.video_tokens(81, h, w)
-    dense, attn = cf.forward_flops(n)
+    # The 14B model of "Video Diffusion Models, in depth", Step 2: 14e9
+    # weights, 40 layers of width 5,120.
+    n = cf.spacetime_tokens(81, h, w)
+    dense, attn = cf.dense_flop(14e9, n), cf.attention_flop(n, 5120, 40)
     share = attn / (dense + attn)
     total = 100 * (dense + attn)
     assert round(share, 2) == float(page_values[f"attn_share_{res}"][0])
@@ -84,7 +86,7 @@ def test_forward_flops_prints(page_values, res, h, w):
 
 
 def test_divided_cost():
-    T, Hp, Wp = cf.token_grid(81, 480, 832)
+    T, Hp, Wp = cf.spacetime_grid(81, 480, 832)
     HW = Hp * Wp
     N = T * HW
     # (HW)*T^2 + T*(HW)^2 = N^2/HW + N^2/T, an identity of the two terms.
@@ -95,8 +97,8 @@ def test_divided_cost():
     assert cf.attention_flops_full(1, H, N, D) == 4 * H * D * cf.full_pairs(N)
     assert (cf.attention_flops_spatial(1, H, T, HW, D) + cf.attention_flops_temporal(1, H, T, HW, D)
             == 4 * H * D * cf.divided_pairs(T, HW))
-    # The page's forward_flops uses dim = heads * head_dim: the same count.
-    assert cf.forward_flops(N, layers=1, dim=H * D)[1] == cf.attention_flops_full(1, H, N, D)
+    # The page's per-layer count uses dim = heads * head_dim: the same count.
+    assert cf.attention_flop(N, H * D, 1) == cf.attention_flops_full(1, H, N, D)
 
 
 def test_probe_token_index(page_values):
