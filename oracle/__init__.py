@@ -262,8 +262,9 @@ def window_attention(q, k, v, grid: Tuple[int, int, int], window: Tuple[int, int
 # Composition of passes
 # ----------------------------------------------------------------------------
 
-def _store(x: np.ndarray, storage: Optional[str]) -> np.ndarray:
-    """Round an intermediate to a storage type (None keeps fp64)."""
+def store(x: np.ndarray, storage: Optional[str]) -> np.ndarray:
+    """Round an intermediate to a storage type: None keeps fp64, "f32" and
+    "bf16" round to nearest even."""
     if storage is None:
         return x
     if storage == "f32":
@@ -287,8 +288,8 @@ def divided(x, grid, order: Sequence[str], rope_split: Optional[Sequence[int]] =
     cur = _f64(x)
     for mode in order:
         qk = rope3d(cur, grid, rope_split, theta) if rope_split is not None else cur
-        qk = _store(qk, storage)
-        cur = _store(attention(qk, qk, cur, grid, mode), storage)
+        qk = store(qk, storage)
+        cur = store(attention(qk, qk, cur, grid, mode), storage)
     return cur
 
 
@@ -296,7 +297,7 @@ def block_input(x_latent, w, grid, heads: int, head_dim: int, rope_split,
                 order=("spatial", "temporal"), theta: float = 10000.0,
                 storage: Optional[str] = None, bias=None) -> np.ndarray:
     """Latent -> patchify -> (RoPE on q, k) -> divided attention, as a chain."""
-    tok = _store(patchify(x_latent, w, bias), storage)
+    tok = store(patchify(x_latent, w, bias), storage)
     B, N, dim = tok.shape
     if dim != heads * head_dim:
         raise OracleError("patchify width must equal heads * head_dim")

@@ -43,3 +43,32 @@ def assert_close(g, r, dtype: str, what: str = ""):
     print(f"[parity] {what}: max_abs={mx:.3e} rel_l1={rl:.3e} (tol {atol:g}, {rel:g})", flush=True)
     assert mx <= atol and rl <= rel, f"{what}: max_abs={mx:.3e} rel_l1={rl:.3e} exceed ({atol}, {rel})"
     return mx, rl
+
+
+def space_then_time_at_positions(x, grid, split, positions, storage=None, theta=10000.0):
+    """The oracle's spatial-then-temporal chain (q = k = RoPE(x), v = x per
+    pass, stored intermediates rounded to ``storage``), evaluated only on the
+    token rows of the given patch positions in every frame.
+
+    The temporal output at a position needs only the spatial outputs at that
+    same position in every frame (its key set), so the chain restricted to
+    rows = {t*HW + p : all t, p in positions} is exact on those rows. Returns
+    (rows, spatial output at rows, chain output at rows). A CPU test checks
+    this against ``oracle.divided`` on small grids.
+    """
+    import oracle
+
+    x = np.asarray(x, dtype=np.float64)
+    T, Hp, Wp = grid
+    HW = Hp * Wp
+    positions = np.asarray(positions, dtype=np.int64)
+    rows = (np.arange(T, dtype=np.int64)[:, None] * HW + positions[None, :]).reshape(-1)
+    r0 = oracle.store(oracle.rope3d(x, grid, split, theta), storage)
+    x1_rows = oracle.store(oracle.attention(r0, r0, x, grid, "spatial", rows=rows), storage)
+    r1_rows = oracle.store(oracle.rope3d_rows(x1_rows, grid, rows, split, theta), storage)
+    x1_full = np.zeros_like(x)
+    r1_full = np.zeros_like(x)
+    x1_full[:, rows] = x1_rows
+    r1_full[:, rows] = r1_rows
+    x2_rows = oracle.store(oracle.attention(r1_full, r1_full, x1_full, grid, "temporal", rows=rows), storage)
+    return rows, x1_rows, x2_rows
