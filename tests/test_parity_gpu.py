@@ -16,7 +16,7 @@ import oracle
 import spacetime_attention_amd as vd
 from synthetic_inputs import (CROSS_WORKLOADS, QKV_WORKLOADS, WORKLOADS, CrossWorkload, QkvWorkload, bf16_bits,
                               bf16_to_f32, draw, round_bf16, sample_rows, small_grid)
-from tests.parity_util import assert_close, to_dev, to_host
+from tests.parity_util import assert_close, space_then_time_at_positions, stats, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -237,16 +237,16 @@ def test_patchify_bias_chunks(C, dout):
 # Full-size workloads, sampled
 # ----------------------------------------------------------------------------
 
-def _sampled_attention(wname, mode, stride, q_scale=1.0):
+def _sampled_attention(wname, mode, stride, q_scale=1.0, offset=None):
     w = WORKLOADS[wname]
     grid = (w.T, w.Hp, w.Wp)
-    _announce(f"{wname} {mode} full size, rows every {stride}")
+    _announce(f"{wname} {mode} full size, rows every {stride}, q/k std {q_scale}")
     d, (q, k, v) = _qkv(w, q_scale)
     got = PASSES[mode](q, k, v, grid)
-    rows = sample_rows(w.N, stride, offset=stride // 3)
+    rows = sample_rows(w.N, stride, offset=stride // 3 if offset is None else offset)
     got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
     ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode, rows=rows)
-    return assert_close(got_rows, ref, "bf16", f"{wname}/{mode}")
+    return assert_close(got_rows, ref, "bf16", f"{wname}/{mode}/std{q_scale}")
 
 
 def test_480p_full_sampled():
@@ -268,7 +268,82 @@ def test_480p_divided_temporal_whole():
 
 
 def test_720p_full_sampled():
-    _sampled_attention("720p_full", "full", 4099)
+    # 259 query rows (every 293rd token from 97, plus the last) of all 40
+    # heads: about 4e11 oracle FLOP.
+    _sampled_attention("720p_full", "full", 293, offset=97)
+
+
+@pytest.mark.parametrize("wname,mode,stride", [("480p_full", "full", 509), ("480p_divided", "spatial", 97)])
+def test_480p_peaky_sampled(wname, mode, stride):
+    # Q and K of standard deviation 4 (logits of standard deviation 16) at
+    # the full size: the reference maximum is raised on many of the 512 key
+    # tiles of a full-attention row, and on the 25 of a frame.
+    _sampled_attention(wname, mode, stride, q_scale=4.0)
+
+
+@pytest.mark.parametrize("wname,mode,stride", [("480p_full", "full", 509), ("480p_divided", "spatial", 97)])
+def test_480p_rising_logits_sampled(wname, mode, stride):
+    # Key norms ramp up 30x along each clip (full) or each clip's token order
+    # (spatial: frame by frame), so the largest score keeps growing across
+    # the key tiles of a row and the reference is raised far into the row.
+    w = WORKLOADS[wname]
+    grid = (w.T, w.Hp, w.Wp)
+    _announce(f"{wname} {mode} rising logits full size, rows every {stride}")
+    d = w.draw_qkv()
+    ramp = (1.0 + 30.0 * np.arange(w.N, dtype=np.float32) / w.N)[None, :, None, None]
+    kb = bf16_bits(d["k"].f32 * ramp)
+    k_f32 = bf16_to_f32(kb).reshape(d["k"].f32.shape)
+    q, v = to_dev(d["q"]), to_dev(d["v"])
+    k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).cuda()
+    got = PASSES[mode](q, k, v, grid)
+    rows = sample_rows(w.N, stride, offset=stride // 2)
+    got_rows = to_host(got[:, torch.from_numpy(rows).cuda()])
+    ref = oracle.attention(d["q"].f32, k_f32, d["v"].f32, grid, mode, rows=rows)
+    assert_close(got_rows, ref, "bf16", f"{wname}/{mode}/rising")
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_explicit_scale(mode, scale):
+    # A positive scale replaces 1/sqrt(head_dim) (0.088 at 128) in every pass.
+    grid = (3, 10, 25)
+    _announce(f"explicit scale {scale} {mode} grid={grid}")
+    w = small_grid("scale", 1, *grid, 2, 128, "bf16", seed=57)
+    d, (q, k, v) = _qkv(w)
+    got = to_host(PASSES[mode](q, k, v, grid, scale=scale))
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode, scale=scale)
+    assert_close(got, ref, "bf16", f"scale{scale}/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["full", "spatial", "temporal"])
+def test_nan_and_inf_propagate(mode):
+    """NaN and Inf inputs are not errors: they reach exactly the outputs whose
+    key sets hold them, as in the oracle (an Inf score makes its row NaN, a
+    -Inf score gets weight 0, NaN or Inf in V reaches that feature of every
+    query that sees the key). Everything else stays finite and in tolerance.
+    Non-finite data cannot make a kernel access memory differently."""
+    grid = (3, 7, 11)
+    N = 231
+    _announce(f"NaN/Inf propagation {mode} grid={grid}")
+    w = small_grid("nonfinite", 1, *grid, 2, 128, "bf16", seed=61)
+    d = w.draw_qkv()
+    q, k, v = (d[n].f32.copy() for n in ("q", "k", "v"))
+    q[0, 40, 0, 5] = np.nan          # one query row of head 0
+    k[0, 100, 1, 7] = np.inf         # one key of head 1: +-Inf scores
+    k[0, 150, 0, 3] = -np.inf        # one key of head 0
+    v[0, 200, 0, 9] = np.nan         # one value feature of head 0
+    v[0, 77, 1, 30] = np.inf         # one value feature of head 1
+    dev = [torch.from_numpy(bf16_bits(t).view(np.int16)).view(torch.bfloat16).cuda() for t in (q, k, v)]
+    got = to_host(PASSES[mode](*dev, grid))
+    ref = oracle.attention(q, k, v, grid, mode)
+    for name, pred in (("nan", np.isnan), ("+inf", np.isposinf), ("-inf", np.isneginf)):
+        assert np.array_equal(pred(got), pred(ref)), f"{mode}: {name} pattern differs"
+    assert np.isnan(ref).any() and np.isinf(ref).any()
+    fin = np.isfinite(ref)
+    assert fin.sum() > 0.3 * ref.size
+    mx, rl = stats(got[fin], ref[fin])
+    print(f"[parity] nonfinite/{mode}: finite part max_abs={mx:.3e} rel_l1={rl:.3e}", flush=True)
+    assert mx <= 2e-2 and rl <= 5e-3
 
 
 # ----------------------------------------------------------------------------
@@ -355,6 +430,19 @@ def test_divided_chain_with_rope_bf16(order):
     assert_close(got, ref, "bf16", f"divided/{'-'.join(order)}+rope")
 
 
+def test_divided_chain_without_rope_bf16():
+    """divided() with no split in bf16: q = k = v = x for each pass, and
+    each pass's output stored in bf16 before the next reads it."""
+    grid = (5, 6, 9)
+    _announce(f"divided chain without RoPE, bf16, grid={grid}")
+    w = small_grid("divided_plain", 1, *grid, 2, 128, "bf16", seed=43)
+    d = w.draw_qkv()
+    for order in (("spatial", "temporal"), ("temporal", "spatial")):
+        got = to_host(vd.divided(to_dev(d["q"]), grid, order=order))
+        ref = oracle.divided(d["q"].f32, grid, order, storage="bf16")
+        assert_close(got, ref, "bf16", f"divided/{'-'.join(order)}")
+
+
 def test_attn_rope_theta_and_scale():
     """Another base and an explicit softmax scale reach the kernel."""
     grid, split = (3, 10, 25), (44, 42, 42)
@@ -417,6 +505,31 @@ def test_block_input_path():
     got_x2 = to_host(x2[:, torch.from_numpy(rows).cuda()])
     assert_close(to_host(x1[:, torch.from_numpy(rows).cuda()]), sp_rows, "bf16", "block/spatial")
     assert_close(got_x2, ref_x2, "bf16", "block/spatial-then-temporal")
+
+
+def test_block_input_divided():
+    """The block-input workload through the binding's own divided() chain at
+    the full 480p size: latent (1,16,21,60,104) -> patchify -> spatial pass
+    on RoPE'd q/k (separate RoPE pass) -> temporal pass with RoPE inside the
+    kernel. The oracle chain rounds the stored tokens, rotated q/k and the
+    spatial output to bf16 as the GPU stores them, and is evaluated at every
+    frame of four patch positions (two interior, the first and the last)."""
+    w = WORKLOADS["block_input"]
+    grid = (w.T, w.Hp, w.Wp)
+    split = w.rope_split
+    _announce("block input through divided(), spatial then temporal, full size")
+    d = w.draw_latent()
+    x, wt = to_dev(d["x"]), to_dev(d["w"])
+    tok = vd.patchify(x, wt, heads=w.heads, head_dim=w.head_dim)
+    x0 = tok.view(1, w.N, w.heads, w.head_dim)
+    got = vd.divided(x0, grid, order=("spatial", "temporal"), split=split)
+    torch.cuda.synchronize()
+    ref_tok = oracle.store(oracle.patchify(d["x"].f32, d["w"].f32), "bf16")
+    HW = w.Hp * w.Wp
+    positions = np.array([0, 777, 1234, HW - 1], dtype=np.int64)
+    rows, _, ref = space_then_time_at_positions(ref_tok.reshape(1, w.N, w.heads, w.head_dim), grid, split,
+                                                positions, storage="bf16")
+    assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", "block/divided()")
 
 
 # ----------------------------------------------------------------------------
