@@ -48,8 +48,6 @@ def _parse():
                    help="skip the oracle timing (profiling runs)")
     p.add_argument("--no-720p", action="store_true",
                    help="skip the full-attention timing at the 14B-shaped 720p size [1,75600,40,128]")
-    p.add_argument("--no-mfma-probe", action="store_true",
-                   help="skip the matrix-core rate probe that runs after the timed steps")
     p.add_argument("--copy-probe", action="store_true",
                    help="run one plain 1 GiB device copy first (HBM counter calibration)")
     return p.parse_args()
@@ -231,8 +229,6 @@ def main():
                                                                         b_temporal)}
     if not args.no_720p:
         result["full_720p"] = bench_full_720p(vd, torch)
-    if not args.no_mfma_probe:
-        result["mfma_ceiling"] = mfma_ceiling(achieved)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(df, wf)
         result["cpu_baseline"]["gpu_over_cpu"] = per_pass["full"]["tflops"] / result["cpu_baseline"]["value"]
@@ -253,18 +249,6 @@ def _warm(torch, fn, min_ms: float = 100.0, at_least: int = 3):
         if n % 4 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-
-
-def mfma_ceiling(achieved_full: float):
-    """The bf16 MFMA rate this device sustains from registers alone (no
-    memory, no softmax), with near-constant and with random full-mantissa
-    operands, measured after the timed steps; and the full pass's rate as a
-    fraction of the random-operand figure."""
-    from spacetime_attention_amd import probe
-    out = {"kernel": "8 chains of v_mfma_f32_32x32x16_bf16 per wave, registers only (libvdit_probe.so)",
-           "near_constant": probe.mfma_rate(False), "random": probe.mfma_rate(True)}
-    out["full_over_random"] = achieved_full / out["random"]["tflops"]
-    return out
 
 
 def bench_temporal_alone(vd, torch, q, k, v, o, grid, nbytes, iters: int = 20):
