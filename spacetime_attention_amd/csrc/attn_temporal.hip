@@ -226,16 +226,16 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
             for (int s2 = 0; s2 < 2; ++s2) {
                 float pv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * s2 + e], c, nm));
-                    ls += pv[e];
-                }
+                for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][8 * s2 + e], c, nm));
                 u32x4 pk;
                 pk[0] = pack_bf16x2(pv[0], pv[1]);
                 pk[1] = pack_bf16x2(pv[2], pv[3]);
                 pk[2] = pack_bf16x2(pv[4], pv[5]);
                 pk[3] = pack_bf16x2(pv[6], pv[7]);
                 pop[qb][kb][s2] = __builtin_bit_cast(bf16x8, pk);
+                // The sum takes the same bf16 weights the V product applies.
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ls = add_bf16_pair(pk[e], ls);
             }
         lsum[qb] = pair_sum(ls);
     }

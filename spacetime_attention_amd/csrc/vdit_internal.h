@@ -29,6 +29,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// acc + lo + hi of a packed bf16 pair (lo in bits 0..15), in fp32: one
+// v_dot2c_f32_bf16 against the pair (1, 1). The probabilities of a softmax
+// are summed this way from the same bf16 values the V product consumes, so
+// the normalisation divides exactly the weights that were applied.
+__device__ __forceinline__ float add_bf16_pair(uint32_t pk, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                           acc, false);
+}
+
 // Maps a hardware workgroup id to a logical tile id so that the workgroups
 // one XCD receives (ids congruent mod 8, dispatched round-robin) form one
 // contiguous run of logical tiles and so share K/V in that XCD's L2.
