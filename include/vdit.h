@@ -181,6 +181,15 @@ vdit_status_t vdit_attn_spatial(const void *q, const void *k, const void *v, voi
  * on-chip memory. q and k in memory are not modified. T as
  * vdit_attn_temporal for the temporal call (<= 64).
  *
+ * Speed: the temporal call takes about half the time of vdit_rope3d on q and
+ * k followed by vdit_attn_temporal (that pass is bound by memory traffic,
+ * and the rotation saves two tensor round trips). The full and spatial
+ * calls are SLOWER than vdit_rope3d followed by the plain call (1.2-1.4x
+ * measured at 480p): every workgroup re-rotates each K tile it reads, which
+ * adds half again to the vector work that already bounds those kernels.
+ * They exist for callers that cannot hold rotated copies of q and k (two
+ * extra tensors, 1.5 GB at the 720p shape); no default path uses them.
+ *
  * Arguments, layouts, limits and errors as vdit_attn_full, plus d_t, d_h,
  * d_w and theta as vdit_rope3d (VDIT_E_ROPE_SPLIT for a bad split,
  * VDIT_E_SHAPE for theta <= 0 or not finite). The angle of each pair is
