@@ -208,7 +208,7 @@ __device__ __forceinline__ void flash_s(const lds_u8 *lds, uint32_t KB0, const u
 template <int D, int QB>
 __device__ __forceinline__ void flash_softmax(f32x16 (&sacc)[2][QB], bf16x8 (&pop)[QB][2][2],
                                               f32x16 (&oacc)[D / 32][QB], float (&mref)[QB], float (&lsum)[QB],
-                                              float c, int kvalid, int half)
+                                              float c, int kvalid, int half, bool first)
 {
     constexpr int DB = D / 32;
     // Keys past the end of the segment (last tile only).
@@ -271,6 +271,17 @@ __device__ __forceinline__ void flash_softmax(f32x16 (&sacc)[2][QB], bf16x8 (&po
                 }
             }
         };
+        if (first) {
+            // Tile 0: the reference starts at the row maximum, so the
+            // probabilities are formed once (against -inf they would all be
+            // infinite and take the slow path below).
+            float mx = sacc[0][qb][0];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][qb][r]);
+            mref[qb] = pair_max(mx) * c;
+        }
         probs();
         if (__builtin_amdgcn_ballot_w64(!(ls <= kTileSumBudget))) {
             float mx = sacc[0][qb][0];
@@ -332,11 +343,16 @@ __device__ __forceinline__ void flash_pv(const lds_u8 *lds, uint32_t VB0, const 
 // against the current reference sum past the budget (or are not finite)
 // raises it, rescales O^T and the running sum (which already hold the
 // earlier blocks) and forms that block again.
-template <int D>
+//
+// On a row's first tile (first) the reference starts at block 0's row
+// maximum instead of -inf. HALF is the form for a last tile whose keys all
+// lie in block 0 (kvalid <= 32): block 1's products and probabilities, all of
+// them for keys past the segment, are left out.
+template <int D, bool HALF>
 __device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, const uint32_t (&kofs)[D / 16],
                                                 const uint32_t (&vofs)[D / 32], const bf16x8 (&qop)[1][D / 16],
                                                 f32x16 (&oacc)[D / 32][1], float (&mref)[1], float (&lsum)[1],
-                                                float c, int kvalid, int half)
+                                                float c, int kvalid, int half, bool first)
 {
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -418,8 +434,16 @@ __device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, 
         }
     }
     mask(0);
+    if (first) {
+        float mx = sb[0][0];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[0][r]);
+        mref[0] = pair_max(mx) * c;
+    }
     // Stage 2: S^T of block 1 under block 0's exponentials.
-    {
+    if constexpr (HALF) {
+        prob_slice(0, 0, 16);
+    } else {
         constexpr int n = 16 / KS;
         bf16x8 ka[2];
         ka[0] = kread(1, 0);
@@ -433,7 +457,7 @@ __device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, 
         }
     }
     finish_block(0);
-    mask(1);
+    if constexpr (!HALF) mask(1);
     // Stage 3: V^T P^T of block 0 (steps 0, 1) under block 1's exponentials.
     {
         constexpr int NM = 2 * DB;
@@ -446,10 +470,11 @@ __device__ __forceinline__ void flash_tile_pipe(const lds_u8 *lds, uint32_t B0, 
             if (m + 1 < NM) va[(m + 1) & 1] = vread((m + 1) / DB, (m + 1) % DB);
             __builtin_amdgcn_sched_barrier(0);
             oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m & 1], pb[0][st], oacc[db][0], 0, 0, 0);
-            prob_slice(1, m, n);
+            if constexpr (!HALF) prob_slice(1, m, n);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    if constexpr (HALF) return;
     finish_block(1);
     // Stage 4: V^T P^T of block 1 (steps 2, 3).
     {
@@ -746,8 +771,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
 
     auto tile = [&](auto bufc, int j) {
         static_assert(PP || QB == 1, "the pipelined tile holds one 32-query block per wave");
-        flash_tile_pipe<D>(decltype(bufc)::value ? lds1 : lds, 0, kofs, vofs, qop, oacc, mref, lsum, c,
-                           Lk - j * kBN, half);
+        const lds_u8 *tb = decltype(bufc)::value ? lds1 : lds;
+        flash_tile_pipe<D, false>(tb, 0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - j * kBN, half, j == 0);
     };
 
     if constexpr (PP) {
@@ -790,7 +815,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
             // Y(j)
             if (j + 2 < ntiles) load_one(krs, koff, (j + 2) * kBN, b2 * S::TILE);
             if (j + 1 < ntiles) load_one(vrs, voff, (j + 1) * kBN, VB + b1 * S::TILE);
-            if (busy) flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, Lk - j * kBN, half);
+            if (busy) flash_softmax<D, QB>(sacc, pop, oacc, mref, lsum, c, Lk - j * kBN, half, j == 0);
             wait_vmem();
             if constexpr (ROPE)
                 if (j + 2 < ntiles) rope_k(lds + b2 * S::TILE);
@@ -840,20 +865,31 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
     // tile from each so that the buffer is a compile-time constant. The
     // other buffer was released by the barrier that ended the previous tile,
     // so the next tile's loads start before this tile's products.
-    for (int j = 0; j < ntiles; j += 2) {
+    // A last tile whose keys all lie in its first 32-key block (the
+    // 1,560-key frames of the spatial pass end with 24) is taken out of the
+    // loop and run in the half form; the loop has already loaded it.
+    const int nmain = Lk - (ntiles - 1) * kBN <= 32 ? ntiles - 1 : ntiles;
+    for (int j = 0; j < nmain; j += 2) {
         if (j + 1 < ntiles) load_tile((j + 1) * kBN, 1);
         if (busy) tile(std::integral_constant<int, 0>{}, j);
         wait_vmem();
         if constexpr (ROPE)
             if (j + 1 < ntiles) rope_k(lds1);
         __syncthreads();
-        if (j + 1 >= ntiles) break;
+        if (j + 1 >= nmain) break;
         if (j + 2 < ntiles) load_tile((j + 2) * kBN, 0);
         if (busy) tile(std::integral_constant<int, 1>{}, j + 1);
         wait_vmem();
         if constexpr (ROPE)
             if (j + 2 < ntiles) rope_k(lds);
         __syncthreads();
+    }
+    if (nmain < ntiles) {
+        const int jl = ntiles - 1;
+        if (busy)
+            flash_tile_pipe<D, true>((jl & 1) ? lds1 : lds, 0, kofs, vofs, qop, oacc, mref, lsum, c, Lk - jl * kBN,
+                                     half, jl == 0);
+        __syncthreads();  // every wave is done with the tile before the buffers stage the output
     }
     }
 
