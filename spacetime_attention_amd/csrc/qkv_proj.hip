@@ -19,9 +19,10 @@
 // head's mean square is a register sum plus one v_permlane32_swap, and each
 // RoPE pair (2j, 2j+1) sits in one lane's consecutive registers.
 //
-// Work layout: a workgroup (4 wavefronts, one per SIMD) owns a 256-channel x
-// 256-token tile; a wavefront owns 128 channels (one head) x 128 tokens, i.e.
-// 4 x 4 blocks and 16 accumulators. K advances in stages of 64: W and x
+// Work layout: a workgroup owns a 256-channel x 256-token tile with 8
+// wavefronts, two per SIMD, so that one's LDS reads, waits and epilogue
+// overlap the other's MFMAs; a wavefront owns 128 channels (one head) x 64
+// tokens, i.e. 4 x 2 blocks and 8 accumulators. K advances in stages of 64: W and x
 // tiles of [256][64] bf16 are filled by buffer loads that write LDS directly
 // and are double-buffered; a chunk-XOR swizzle keeps the operand reads
 // (32 rows, one 16-byte chunk each) free of bank conflicts. Rows past the end
@@ -36,7 +37,7 @@ namespace {
 constexpr int kTileC = 256;  // channels per workgroup
 constexpr int kTileT = 256;  // tokens per workgroup
 constexpr int kBK = 64;      // k per LDS stage
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kGroupT = 8;   // token tiles per ordering group
 constexpr int kRowBytes = kBK * 2;                  // 128 bytes of one tile row
 constexpr int kTileBytes = kTileC * kRowBytes;      // 32 KB (W or x tile)
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
-    const int wc = wave & 1, wt = wave >> 1;  // channel half, token half of the tile
+    const int wc = wave & 1, wt = wave >> 1;  // channel half, token quarter of the tile
 
     // Buffer descriptors from the tile's first W row and first x row; the
     // sizes end at the last row of each matrix.
@@ -120,31 +121,30 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     };
 
     // Operand read offsets for k-step 0 of stage 0: W row wc*128 + col (+32
-    // per channel block), x row wt*128 + col (+32 per token block); the
+    // per channel block), x row wt*64 + col (+32 per token block); the
     // swizzle depends on the row only through col.
     uint32_t aofs[4], bofs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         aofs[ks] = (uint32_t)((wc * 128 + col) * kRowBytes + swz(col, 2 * ks + half) * 16);
-        bofs[ks] = (uint32_t)(kTileBytes + (wt * 128 + col) * kRowBytes + swz(col, 2 * ks + half) * 16);
+        bofs[ks] = (uint32_t)(kTileBytes + (wt * 64 + col) * kRowBytes + swz(col, 2 * ks + half) * 16);
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = (f32x16){};
+        for (int tb = 0; tb < 2; ++tb) acc[cb][tb] = (f32x16){};
 
     const int nk = dim / kBK;
     auto stage = [&](auto stc) {
         constexpr uint32_t S0 = decltype(stc)::value * kStageBytes;
-        bf16x8 a[2][4], b[2][4];
+        bf16x8 a[2][4], b[2][2];
         auto rd = [&](int ks, int slot) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                a[slot][i] = *(const lds_bf16x8 *)(lds + aofs[ks] + (S0 + i * 32 * kRowBytes));
-                b[slot][i] = *(const lds_bf16x8 *)(lds + bofs[ks] + (S0 + i * 32 * kRowBytes));
-            }
+            for (int i = 0; i < 4; ++i) a[slot][i] = *(const lds_bf16x8 *)(lds + aofs[ks] + (S0 + i * 32 * kRowBytes));
+#pragma unroll
+            for (int i = 0; i < 2; ++i) b[slot][i] = *(const lds_bf16x8 *)(lds + bofs[ks] + (S0 + i * 32 * kRowBytes));
         };
         rd(0, 0);
 #pragma unroll
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
+                for (int tb = 0; tb < 2; ++tb)
                     acc[cb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][cb], b[ks & 1][tb],
                                                                          acc[cb][tb], 0, 0, 0);
         }
@@ -189,7 +189,9 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     // Lane channels within the head: cb*32 + 8*r4 + 4*half + e, e < 4 (the
     // accumulator register 4*r4 + e of block cb). Every 32-token block is
     // finished in registers, staged through this wave's own LDS region and
-    // written as whole 256-byte token rows.
+    // written as whole 256-byte token rows. Bias and gain are read per
+    // block (from L2) rather than held across both blocks, which would
+    // spill at two waves per SIMD.
     const int cw = c0 + wc * 128;
     if (cw >= 3 * dim) return;
     const int which = cw / dim;             // 0 Q, 1 K, 2 V
@@ -199,16 +201,6 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     const bool rot = which < 2 && rope.on;
     const int HW = g.Hp * g.Wp;
 
-    // Bias and gain of the lane's 64 channels as packed bf16 pairs.
-    u32x2 bw[4][4], gw[4][4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int ch = cb * 32 + 8 * r4 + 4 * half;
-            bw[cb][r4] = bias ? *(const u32x2 *)(bias + cw + ch) : (u32x2){0u, 0u};
-            gw[cb][r4] = gain ? *(const u32x2 *)(gain + hc + ch) : (u32x2){0x3f803f80u, 0x3f803f80u};
-        }
     auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
     auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
     // RoPE: pair rp of block cb is channel pair p = cb*16 + 4*(rp/2) + rp%2
@@ -218,8 +210,8 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     lds_u8 *stg = lds + wave * 32 * kPitch;
 
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const int mt = t0 + wt * 128 + tb * 32;  // first token row of the block
+    for (int tb = 0; tb < 2; ++tb) {
+        const int mt = t0 + wt * 64 + tb * 32;  // first token row of the block
         const int m = mt + col;
         float y[4][16];
         float ss = 0.f;
@@ -227,7 +219,9 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const float b4[4] = {lo(bw[cb][r4][0]), hi(bw[cb][r4][0]), lo(bw[cb][r4][1]), hi(bw[cb][r4][1])};
+                const int ch = cb * 32 + 8 * r4 + 4 * half;
+                const u32x2 bw = bias ? *(const u32x2 *)(bias + cw + ch) : (u32x2){0u, 0u};
+                const float b4[4] = {lo(bw[0]), hi(bw[0]), lo(bw[1]), hi(bw[1])};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     y[cb][4 * r4 + e] = acc[cb][tb][4 * r4 + e] + b4[e];
@@ -240,8 +234,9 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const float g4[4] = {lo(gw[cb][r4][0]), hi(gw[cb][r4][0]), lo(gw[cb][r4][1]),
-                                         hi(gw[cb][r4][1])};
+                    const int ch = cb * 32 + 8 * r4 + 4 * half;
+                    const u32x2 gw = *(const u32x2 *)(gain + hc + ch);
+                    const float g4[4] = {lo(gw[0]), hi(gw[0]), lo(gw[1]), hi(gw[1])};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) y[cb][4 * r4 + e] *= sc * g4[e];
                 }
