@@ -681,13 +681,12 @@ QKV_SMALL = [
     ("plain_projection", 1, (1, 16, 16), 2, 128, "bf16", None, True, False),
     ("tiny_width_f32", 1, (4, 8, 8), 2, 32, "f32", (12, 10, 10), True, True),
     ("f32_d128", 2, (2, 3, 5), 2, 128, "f32", (44, 42, 42), False, True),
-    # Splits other than (44, 42, 42) through the rotation table, one with no
-    # time pairs.
+    # Splits other than (44, 42, 42), one with no time pairs.
     ("split_64_32_32", 1, (3, 6, 10), 2, 128, "bf16", (64, 32, 32), True, True),
     ("split_0_64_64", 1, (2, 5, 12), 2, 128, "bf16", (0, 64, 64), False, True),
-    # A grid whose (cos, sin) table (22 + 2*21 + 200*21 entries) exceeds the
-    # kernel's LDS table: the rotation angles are evaluated directly.
-    ("wide_grid_direct_rope", 1, (1, 2, 200), 2, 128, "bf16", (44, 42, 42), True, True),
+    # A wide grid: w positions up to 199, so the w-axis angles reach many
+    # revolutions before their reduction.
+    ("wide_grid_rope", 1, (1, 2, 200), 2, 128, "bf16", (44, 42, 42), True, True),
 ]
 
 
