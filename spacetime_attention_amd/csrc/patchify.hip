@@ -10,19 +10,25 @@
 // which is the Conv3d weight [Dout][C][pt][ph][pw] read as a [Dout][K]
 // row-major matrix. Output rows are token-major, m = b*N + (t*Hp+h)*Wp + w.
 //
-// bf16 path (v_mfma_f32_32x32x16_bf16, fp32 accumulation): a workgroup owns
-// kTok tokens; it gathers their [kTok][K] patch matrix into LDS once and
-// sweeps all output channels in chunks of 128, each wave computing a
-// 32-channel x kTok-token block of C^T = W A^T with W and the bias read
-// straight from global (they are small and stay in L2), one chunk ahead.
-// Each chunk is staged through LDS (two alternating buffers, one barrier per
-// chunk) and written as whole 256-byte row runs: at K = 64 the kernel writes
-// 24x more bytes than it reads, so coalesced stores set its speed. LDS is
-// sized to the actual patch length so several workgroups share a CU.
+// bf16 paths (fp32 accumulation). At K = 64 the kernel writes 24x more
+// bytes than it reads, so the store stream sets its speed.
+//  - K <= 64 (patchify_ldsw_bf16, below): W and bias in LDS, each wavefront
+//    free of barriers after start-up, so stores stream without a break.
+//  - Longer patches (patchify_bf16_kernel, v_mfma_f32_32x32x16_bf16): a
+//    workgroup owns kTok tokens; it gathers their [kTok][K] patch matrix
+//    into LDS once and
+//    sweeps all output channels in chunks of 128, each wave computing a
+//    32-channel x kTok-token block of C^T = W A^T with W and the bias read
+//    straight from global (they are small and stay in L2), one chunk ahead.
+//    Each chunk is staged through LDS (two alternating buffers, one barrier
+//    per chunk) and written as whole 256-byte row runs. LDS is sized to the
+//    actual patch length so several workgroups share a CU.
 //
 // fp32 path: one thread per output element, a plain dot product (for the
 // small fp32 workloads that must agree with fp64 to 1e-5).
 #include "vdit_internal.h"
+
+#include <type_traits>
 
 namespace vdit {
 namespace {
@@ -281,6 +287,260 @@ __global__ __launch_bounds__(256) void patchify_f32_kernel(const float *__restri
     tok[idx] = acc;
 }
 
+// ---- Patch lengths up to 64: W in LDS, wavefronts without barriers ----
+//
+// A workgroup owns kPWaves * 64 tokens (64 per wavefront) x kPCh output
+// channels.
+// It copies its kPCh rows of W and their bias into LDS once, while each
+// wavefront gathers its 64 tokens' patch values straight into the B operands
+// of v_mfma_f32_16x16x32_bf16 (tokens as columns); after one barrier no
+// wavefront touches global memory again except to store. A wavefront sweeps
+// the channels 64 at a time: A operands (channels as rows) and bias come
+// from LDS, the 16 x 16 results start from the bias, go to bf16, are staged
+// through the wavefront's own LDS rows and leave as 128-byte row pieces.
+// Vector-memory completions are counted in issue order, so loads issued
+// after stores would wait for those stores; with no loads after the first
+// store, the stores stream out at the rate HBM takes them, which at K = 64
+// (24x more bytes written than read) sets the kernel's pace.
+//
+// 16x16x32 operand layout: lane l holds 8 consecutive-k values of row
+// (A) or column (B) l % 16, k group l / 16; the result lane l holds rows
+// 4*(l/16) .. +3 of column l % 16.
+constexpr int kPTok = 64;       // tokens per wavefront: four 16-token blocks
+constexpr int kPWaves = 8;      // wavefronts per workgroup, two per SIMD
+constexpr int kPCh = 384;       // output channels per workgroup: six 64-channel steps
+constexpr int kPPitch = 144;    // bytes per LDS row of W and of the staged output (128 + 16: no bank conflicts)
+constexpr int kPLdsW = kPCh * kPPitch;
+constexpr int kPLdsBias = kPCh * 2;
+constexpr int kPLdsStage = kPWaves * kPTok * kPPitch;
+constexpr int kPLds = kPLdsW + kPLdsBias + kPLdsStage;
+constexpr int kPThreads = 64 * kPWaves;
+
+// KS: 32-wide k steps (1 or 2). FAST: bricks two wide with an even latent
+// width, so each (kw = 0, 1) pair is one aligned 4-byte load. KVEC: K a
+// multiple of 8, so W rows are read in 16-byte pieces.
+//
+// The start-up loads are unconditional (addresses clamped into range, the
+// values zeroed afterwards where they fall outside), so that no lane-
+// dependent branch separates them and each wait covers exactly the loads it
+// needs.
+template <int KS, bool FAST, bool KVEC>
+__global__ __launch_bounds__(kPThreads) void patchify_ldsw_bf16(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w,
+                                                          const uint16_t *__restrict__ bias,
+                                                          uint16_t *__restrict__ tok, PatchGeom g, int K,
+                                                          int ngroups)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+    lds_u8 *wl = (lds_u8 *)dyn_lds;
+    lds_u8 *bl = wl + kPLdsW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, kg = lane >> 4;
+    lds_u8 *stg = bl + kPLdsBias + wave * kPTok * kPPitch;
+    const int64_t N = (int64_t)g.T * g.Hp * g.Wp;
+    const int64_t M = (int64_t)g.B * N;
+    const int64_t sb = blockIdx.x / ngroups;
+    const int ch0 = (int)(blockIdx.x % ngroups) * kPCh;
+    const int64_t m0 = (sb * kPWaves + wave) * kPTok;
+
+    // W rows ch0 .. ch0 + kPCh - 1 for LDS: 16-byte chunk q of row r holds
+    // k = 8q .. 8q+7 (zero past K and past Dout); eight threads per row. All
+    // loads are issued before any LDS write (and before the gather's loads),
+    // so their latencies overlap.
+    constexpr int kFill = kPCh * 8 / kPThreads;
+    static_assert(kPCh * 8 % kPThreads == 0 && kPCh <= kPThreads,
+                  "W rows fill whole rounds of the workgroup; one bias per thread");
+    u32x4 wv[kFill];
+    if constexpr (KVEC) {
+#pragma unroll
+        for (int it = 0; it < kFill; ++it) {
+            const int c = tid + kPThreads * it, r = c >> 3, q = c & 7, ch = ch0 + r;
+            const bool in = ch < g.Dout && 8 * q < K;
+            wv[it] = *(const u32x4 *)(w + (int64_t)min(ch, g.Dout - 1) * K + (in ? 8 * q : 0));
+            if (!in) wv[it] = (u32x4){0u, 0u, 0u, 0u};
+        }
+    } else {
+        // W rows not 16-byte aligned: element by element, straight to LDS.
+        for (int c = tid; c < kPCh * 8; c += kPThreads) {
+            const int r = c >> 3, q = c & 7, ch = ch0 + r;
+            uint16_t e8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                e8[e] = (ch < g.Dout && 8 * q + e < K) ? w[(int64_t)ch * K + 8 * q + e] : 0;
+            *(__attribute__((address_space(3))) u32x4 *)(wl + r * kPPitch + q * 16) = __builtin_bit_cast(u32x4, e8);
+        }
+    }
+
+
+    // B operands: token block tb, k step s holds patch values k = 32*s +
+    // 8*kg .. +8 of token m0 + 16*tb + col (zero past K and past M).
+    //
+    // Patch value k sits at latent offset poff(k) from the token's brick
+    // corner; the lane's offsets are the same for all four tokens it
+    // gathers, so they are formed once, by carrying through (c, i, j, kw)
+    // rather than dividing. FAST reads (kw = 0, 1) pairs: pair index
+    // r = k / 2 = (c*pt + i)*ph + j.
+    constexpr int NV = FAST ? 4 : 8;  // loads per k step
+    int poff[KS][NV];
+    {
+        const int64_t sc = (int64_t)g.Tl * g.Hl * g.Wl, si = (int64_t)g.Hl * g.Wl;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            // First index of this lane's run, split once.
+            int k0 = 32 * s2 + 8 * kg;
+            int kw = 0, j, ii, c;
+            if constexpr (FAST) {
+                const int r0 = k0 / 2;
+                j = r0 % g.ph;
+                ii = (r0 / g.ph) % g.pt;
+                c = r0 / (g.ph * g.pt);
+            } else {
+                kw = k0 % g.pw;
+                j = (k0 / g.pw) % g.ph;
+                ii = (k0 / (g.pw * g.ph)) % g.pt;
+                c = k0 / (g.pw * g.ph * g.pt);
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int kk = FAST ? k0 + 2 * v : k0 + v;
+                poff[s2][v] = kk < K ? (int)(c * sc + ii * si + (int64_t)j * g.Wl + kw) : -1;
+                if (!FAST && ++kw < g.pw) continue;
+                kw = 0;
+                if (++j == g.ph) {
+                    j = 0;
+                    if (++ii == g.pt) {
+                        ii = 0;
+                        ++c;
+                    }
+                }
+            }
+        }
+    }
+    // The wavefront's first token is split once (uniform); the lane's tokens
+    // m0 + col + 16*tb then follow by carrying through (w, h, t, b).
+    int64_t bb = m0 / N;
+    int nn = (int)(m0 - bb * N) + col;
+    while (nn >= N) {
+        nn -= (int)N;
+        ++bb;
+    }
+    const int HWp = g.Hp * g.Wp;
+    int tt = nn / HWp, hh = (nn - tt * HWp) / g.Wp;
+    int ww = nn - tt * HWp - hh * g.Wp;
+    // Brick corners of the lane's four tokens, then every load, then the
+    // operands: no load waits on another.
+    const uint16_t *xbs[4];
+    bool live[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        live[tb] = m0 + 16 * tb + col < M;
+        // Tokens past the end read from the start of the latent (one clip
+        // spans every patch offset) and are zeroed below.
+        xbs[tb] = live[tb] ? x + (((bb * g.C) * g.Tl + (int64_t)tt * g.pt) * g.Hl + (int64_t)hh * g.ph) * g.Wl +
+                                 (int64_t)ww * g.pw
+                           : x;
+        // Next token of this lane: 16 further along w.
+        ww += 16;
+        while (ww >= g.Wp) {
+            ww -= g.Wp;
+            if (++hh == g.Hp) {
+                hh = 0;
+                if (++tt == g.T) {
+                    tt = 0;
+                    ++bb;
+                }
+            }
+        }
+    }
+    // Offsets past K (marked -1) read the brick corner and are zeroed
+    // below, so no load is branched around.
+    // This thread's bias value for LDS (read now, zeroed at its LDS write).
+    const uint16_t bv16 = bias ? bias[min(ch0 + tid, g.Dout - 1)] : (uint16_t)0;
+    using raw_t = std::conditional_t<FAST, uint32_t, uint16_t>;
+    raw_t raw[4][KS][NV];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int o = poff[s2][v];
+                raw[tb][s2][v] = *(const raw_t *)(xbs[tb] + (o < 0 ? 0 : o));
+            }
+    if constexpr (KVEC) {
+#pragma unroll
+        for (int it = 0; it < kFill; ++it) {
+            const int c = tid + kPThreads * it;
+            *(__attribute__((address_space(3))) u32x4 *)(wl + (c >> 3) * kPPitch + (c & 7) * 16) = wv[it];
+        }
+    }
+    if (tid < kPCh)
+        *(__attribute__((address_space(3))) uint16_t *)(bl + 2 * tid) = ch0 + tid < g.Dout ? bv16 : (uint16_t)0;
+    __syncthreads();
+    if (m0 >= M) return;  // past the last token; no barrier follows
+    bf16x8 bop[4][KS];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+            if constexpr (FAST) {
+                u32x4 u;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) u[v] = (poff[s2][v] < 0 || !live[tb]) ? 0u : raw[tb][s2][v];
+                bop[tb][s2] = __builtin_bit_cast(bf16x8, u);
+            } else {
+                uint16_t e16[8];
+#pragma unroll
+                for (int v = 0; v < 8; ++v) e16[v] = (poff[s2][v] < 0 || !live[tb]) ? (uint16_t)0 : raw[tb][s2][v];
+                bop[tb][s2] = __builtin_bit_cast(bf16x8, e16);
+            }
+        }
+
+    const int nsteps = min(kPCh / 64, (g.Dout - ch0 + 63) / 64);
+    for (int st = 0; st < nsteps; ++st) {
+        // Result (cb, tb): lane holds channels 64*st + 16*cb + 4*kg + e of
+        // token 16*tb + col; staged at that token's row, byte 32*cb + 8*kg.
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int r = 64 * st + 16 * cb;
+            bf16x8 a[KS];
+#pragma unroll
+            for (int s2 = 0; s2 < KS; ++s2)
+                a[s2] = *(const __attribute__((address_space(3))) bf16x8 *)(wl + (r + col) * kPPitch +
+                                                                             (4 * s2 + kg) * 16);
+            const u32x2 bw = *(const __attribute__((address_space(3))) u32x2 *)(bl + 2 * (r + 4 * kg));
+            const f32x4 acc0 = (f32x4){__uint_as_float(bw[0] << 16), __uint_as_float(bw[0] & 0xffff0000u),
+                                       __uint_as_float(bw[1] << 16), __uint_as_float(bw[1] & 0xffff0000u)};
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                f32x4 acc = acc0;
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s2], bop[tb][s2], acc, 0, 0, 0);
+                u32x2 pk;
+                pk[0] = pack_bf16x2(acc[0], acc[1]);
+                pk[1] = pack_bf16x2(acc[2], acc[3]);
+                *(__attribute__((address_space(3))) u32x2 *)(stg + (16 * tb + col) * kPPitch + 32 * cb + 8 * kg) = pk;
+            }
+        }
+        // The rows are this wavefront's own: its LDS writes complete in
+        // order before the reads below.
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        // Rows back out: 8 lanes per 128-byte row piece, 8 rows per read.
+        const int chs = ch0 + 64 * st + 8 * (lane & 7);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int row = 8 * it + (lane >> 3);
+            const u32x4 d = *(const __attribute__((address_space(3))) u32x4 *)(stg + row * kPPitch + (lane & 7) * 16);
+            const int64_t m = m0 + row;
+            if (m < M && chs < g.Dout) *(u32x4 *)(tok + m * g.Dout + chs) = d;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, void *tok, const PatchGeom &g,
@@ -289,6 +549,30 @@ hipError_t launch_patchify_bf16(const void *x, const void *w, const void *bias, 
     const int Kp = (K + 15) / 16 * 16;
     if (Kp > kMaxK || g.Dout % 8) return hipErrorInvalidValue;
     const int64_t M = (int64_t)g.B * g.T * g.Hp * g.Wp;
+    if (K <= 64 && (int64_t)g.T * g.Hp * g.Wp < INT32_MAX && (int64_t)g.C * g.Tl * g.Hl * g.Wl < INT32_MAX) {
+        // One workgroup per kPWaves * 64 tokens x kPCh channels (clip length and one
+        // clip's latent addressed with 32-bit offsets).
+        const int ngroups = (g.Dout + kPCh - 1) / kPCh;
+        const int64_t wgs = (M + kPTok * kPWaves - 1) / (kPTok * kPWaves) * ngroups;
+        if (wgs > 0 && wgs <= UINT32_MAX) {
+            const bool fast = g.pw == 2 && (g.Wl & 1) == 0;
+            auto go_w = [&](auto kernel) {
+                const hipError_t e =
+                    hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kPLds);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL(kernel, dim3((uint32_t)wgs), dim3(kPThreads), kPLds, s, (const uint16_t *)x,
+                                   (const uint16_t *)w, (const uint16_t *)bias, (uint16_t *)tok, g, K, ngroups);
+                return hipGetLastError();
+            };
+            const bool kvec = K % 8 == 0;
+            if (K <= 32) {
+                if (fast) return kvec ? go_w(patchify_ldsw_bf16<1, true, true>) : go_w(patchify_ldsw_bf16<1, true, false>);
+                return kvec ? go_w(patchify_ldsw_bf16<1, false, true>) : go_w(patchify_ldsw_bf16<1, false, false>);
+            }
+            if (fast) return kvec ? go_w(patchify_ldsw_bf16<2, true, true>) : go_w(patchify_ldsw_bf16<2, true, false>);
+            return kvec ? go_w(patchify_ldsw_bf16<2, false, true>) : go_w(patchify_ldsw_bf16<2, false, false>);
+        }
+    }
     const dim3 grid((uint32_t)((M + kTok - 1) / kTok), kChunkSplit);
     const size_t lds = (size_t)kTok * (4 * (kOut + 8) + (Kp + 8)) * 2;
     auto go = [&](auto kernel) {

@@ -233,6 +233,43 @@ def test_patchify_bias_chunks(C, dout):
     assert_close(got, ref, "bf16", f"patchify/C{C}/dout{dout}")
 
 
+@pytest.mark.parametrize("C,pt,ph,pw,dout,B", [
+    (4, 1, 2, 2, 256, 1),    # K = 16: one 32-wide k step, half of it padding
+    (8, 1, 2, 2, 128, 2),    # K = 32: exactly one k step; two clips
+    (3, 1, 2, 2, 448, 1),    # K = 12: W rows not a multiple of 8 elements; 7 channel steps
+    (16, 2, 2, 2, 256, 1),   # K = 128: beyond the per-wavefront kernel's two k steps
+    (8, 1, 2, 6, 384, 1),    # K = 96, six-wide bricks: general gather of the chunked kernel
+])
+def test_patchify_patch_lengths(C, pt, ph, pw, dout, B):
+    # Patch lengths on both sides of 64 (the largest the per-wavefront kernel
+    # takes) and of 32, over a 2 x 5 x 7 token grid: 70 tokens, so the second
+    # 64-token block is ragged.
+    _announce(f"patchify patch length {C * pt * ph * pw}: C={C} brick {pt}x{ph}x{pw} dout={dout} B={B}")
+    d = draw(44 + C + pw, [("x", (B, C, 2 * pt, 5 * ph, 7 * pw), 1.0), ("w", (dout, C, pt, ph, pw), 0.05),
+                           ("b", (dout,), 0.1)], "bf16")
+    x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
+    got = to_host(vd.patchify(x, wt, b, heads=dout // 64, head_dim=64))
+    ref = oracle.patchify(d["x"].f32, d["w"].f32, d["b"].f32)
+    assert got.shape == ref.shape == (B, 70, dout)
+    assert_close(got, ref, "bf16", f"patchify/K{C * pt * ph * pw}")
+
+
+def test_patchify_480p_frames():
+    # The 480p block input at full size: latent (1,16,21,60,104) -> 32,760
+    # tokens of 1,536 (the last 64-token block holds 56). Three whole latent
+    # frames are checked against the oracle run on those frames alone
+    # (patchify is local in t).
+    _announce("patchify 480p full size: latent (1,16,21,60,104) -> [1,32760,1536], frames 0, 9, 20")
+    d = draw(47, [("x", (1, 16, 21, 60, 104), 1.0), ("w", (1536, 16, 1, 2, 2), 0.05), ("b", (1536,), 0.1)],
+             "bf16")
+    x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
+    got = vd.patchify(x, wt, b, heads=12, head_dim=128)
+    hw = 30 * 52
+    for t in (0, 9, 20):
+        ref = oracle.patchify(d["x"].f32[:, :, t:t + 1], d["w"].f32, d["b"].f32)
+        assert_close(to_host(got[:, t * hw:(t + 1) * hw]), ref, "bf16", f"patchify/480p/frame{t}")
+
+
 # ----------------------------------------------------------------------------
 # Full-size workloads, sampled
 # ----------------------------------------------------------------------------
