@@ -339,8 +339,12 @@ __global__ __launch_bounds__(kPThreads) void patchify_ldsw_bf16(const uint16_t *
     lds_u8 *stg = bl + kPLdsBias + wave * kPTok * kPPitch;
     const int64_t N = (int64_t)g.T * g.Hp * g.Wp;
     const int64_t M = (int64_t)g.B * N;
-    const int64_t sb = blockIdx.x / ngroups;
-    const int ch0 = (int)(blockIdx.x % ngroups) * kPCh;
+    // Workgroups are numbered so that the channel groups of one token block
+    // run on one XCD (ids congruent mod 8 share an XCD): the latent rows the
+    // first of them gathers are then in that XCD's L2 for the others.
+    const uint32_t wid = xcd_contiguous(blockIdx.x, gridDim.x);
+    const int64_t sb = wid / ngroups;
+    const int ch0 = (int)(wid % ngroups) * kPCh;
     const int64_t m0 = (sb * kPWaves + wave) * kPTok;
 
     // W rows ch0 .. ch0 + kPCh - 1 for LDS: 16-byte chunk q of row r holds
