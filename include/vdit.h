@@ -146,7 +146,7 @@ vdit_status_t vdit_rope3d(const void *x, void *y, int B, int heads, int T, int H
  * q, k, v, o : [B, N, heads, head_dim], N = T*Hp*Wp. o may not overlap q, k
  *              or v (VDIT_E_ALIAS).
  * scale      : softmax scale; <= 0 selects 1/sqrt(head_dim).
- * head_dim   : VDIT_BF16: 64 or 128; VDIT_F32: 32, 64 or 128
+ * head_dim   : 32, 64 or 128 (VDIT_BF16 and VDIT_F32)
  *              (else VDIT_E_HEAD_DIM).
  * Size limit : VDIT_BF16 needs one batch's tensor, N*heads*head_dim*2 bytes,
  *              below 2 GiB (else VDIT_E_SHAPE); 720p at 40 heads is 774 MB.
@@ -218,7 +218,7 @@ vdit_status_t vdit_attn_temporal_rope(const void *q, const void *k, const void *
  * are the T tokens (t', h, w), t' = 0..T-1 (same passages; the (HW)*T^2
  * term). Consecutive keys of a sequence are Hp*Wp tokens apart in the
  * token-major layout; the kernel reads them in place. Arguments as
- * vdit_attn_full; head_dim: VDIT_BF16 64 or 128, VDIT_F32 32, 64 or 128.
+ * vdit_attn_full; head_dim 32, 64 or 128.
  * T <= 64 for VDIT_BF16 and T <= 256 for VDIT_F32 (else VDIT_E_SHAPE).
  */
 vdit_status_t vdit_attn_temporal(const void *q, const void *k, const void *v, void *o,

@@ -964,6 +964,13 @@ hipError_t launch_flash_bf16(const void *q, const void *k, const void *v, void *
         if (pass == 1) return launch<64, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
         return launch<64, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
     }
+    if (D == 32) {
+        // A 64-key tile of 32-wide rows is 4 KB, half a 1 KB load per wave of
+        // the 8-wave ping-pong; every pass takes the 4-wave pipelined tile.
+        if (pass == 0) return launch<32, 1, kSpatialWaves, 0>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        if (pass == 1) return launch<32, 1, kSpatialWaves, 1>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+        return launch<32, 1, kSpatialWaves, 2>(q, k, v, o, nseg, L, Lk, heads, scale_log2e, s);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -979,6 +986,10 @@ hipError_t launch_flash_rope_bf16(const void *q, const void *k, const void *v, v
         if (pass == 0) return launch<64, 1, kFullWaves, 4>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
         if (pass == 1) return launch<64, 1, kSpatialWaves, 5>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
     }
+    if (D == 32) {
+        if (pass == 0) return launch<32, 1, kSpatialWaves, 4>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
+        if (pass == 1) return launch<32, 1, kSpatialWaves, 5>(q, k, v, o, nseg, L, Lk, heads, c, s, WinGeom{}, rope);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -992,6 +1003,7 @@ hipError_t launch_window_bf16(const void *q, const void *k, const void *v, void 
     const int Lmax = g.wt * g.wh * g.ww;  // extents are already clipped to the grid
     if (D == 128) return launch<128, 1, kSpatialWaves, 3>(q, k, v, o, nseg, Lmax, Lmax, heads, scale_log2e, s, wg);
     if (D == 64) return launch<64, 1, kSpatialWaves, 3>(q, k, v, o, nseg, Lmax, Lmax, heads, scale_log2e, s, wg);
+    if (D == 32) return launch<32, 1, kSpatialWaves, 3>(q, k, v, o, nseg, Lmax, Lmax, heads, scale_log2e, s, wg);
     return hipErrorInvalidValue;
 }
 

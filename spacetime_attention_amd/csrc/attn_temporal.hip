@@ -316,12 +316,16 @@ hipError_t dispatch(const void *q, const void *k, const void *v, void *o, int B,
     if (T <= 24) {
         if (D == 128) return launch<128, 1, 24, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
         if (D == 64) return launch<64, 1, 24, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        // 32-wide rows: one 1 KB load is 16 rows, so the Q and K slices are 32.
+        if (D == 32) return launch<32, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
     } else if (T <= 32) {
         if (D == 128) return launch<128, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
         if (D == 64) return launch<64, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        if (D == 32) return launch<32, 1, 32, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
     } else if (T <= 64) {
         if (D == 128) return launch<128, 2, 64, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
         if (D == 64) return launch<64, 2, 64, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
+        if (D == 32) return launch<32, 2, 64, ROPE>(q, k, v, o, B, heads, T, HW, c, s, fr);
     }
     return hipErrorInvalidValue;
 }

@@ -60,8 +60,7 @@ vdit_status_t attn(const void *q, const void *k, const void *v, void *o, int B, 
     uint64_t elems = n_tok;
     if (!mul_ok(elems, B) || !mul_ok(elems, heads) || !mul_ok(elems, D)) return VDIT_E_SHAPE;
     const uint64_t bytes = elems * (uint64_t)esize(dt);
-    if (dt == VDIT_BF16 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
-    if (dt == VDIT_F32 && D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    if (D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
     if (mode == kTemporal && T > (dt == VDIT_BF16 ? 64 : 256)) return VDIT_E_SHAPE;
     // Workgroup counts must fit a 1-D grid.
     if ((uint64_t)B * heads * n_tok > (uint64_t)UINT32_MAX * 32) return VDIT_E_SHAPE;
@@ -168,8 +167,7 @@ vdit_status_t vdit_attn_cross(const void *q, const void *k, const void *v, void 
     if (dtype != VDIT_BF16 && dtype != VDIT_F32) return VDIT_E_DTYPE;
     if (B <= 0 || heads <= 0 || Nq <= 0 || Nk <= 0 || head_dim <= 0) return VDIT_E_SHAPE;
     const int D = head_dim;
-    if (dtype == VDIT_BF16 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
-    if (dtype == VDIT_F32 && D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    if (D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
     uint64_t qe = 1, ke = 1;
     if (!mul_ok(qe, B) || !mul_ok(qe, Nq) || !mul_ok(qe, heads) || !mul_ok(qe, D)) return VDIT_E_SHAPE;
     if (!mul_ok(ke, B) || !mul_ok(ke, Nk) || !mul_ok(ke, heads) || !mul_ok(ke, D)) return VDIT_E_SHAPE;
@@ -197,8 +195,7 @@ vdit_status_t vdit_attn_window(const void *q, const void *k, const void *v, void
     if (B <= 0 || heads <= 0 || T <= 0 || Hp <= 0 || Wp <= 0 || head_dim <= 0 || wt <= 0 || wh <= 0 || ww <= 0)
         return VDIT_E_SHAPE;
     const int D = head_dim;
-    if (dtype == VDIT_BF16 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
-    if (dtype == VDIT_F32 && D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
+    if (D != 32 && D != 64 && D != 128) return VDIT_E_HEAD_DIM;
     uint64_t n_tok = 1;
     if (!mul_ok(n_tok, T) || !mul_ok(n_tok, Hp) || !mul_ok(n_tok, Wp)) return VDIT_E_SHAPE;
     if (n_tok > (uint64_t)INT32_MAX) return VDIT_E_SHAPE;

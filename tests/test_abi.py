@@ -60,7 +60,7 @@ def test_attention_argument_errors(lib, fn):
     assert call(T=1 << 16, Hp=1 << 16, Wp=1 << 16) == 2  # overflow
     assert call(T=64, Hp=256, Wp=256, heads=16) == 2     # one batch over 2 GiB in bf16
     assert call(D=96) == 3                        # VDIT_E_HEAD_DIM
-    assert call(D=32) == 3                        # bf16 supports 64 and 128
+    assert call(D=48) == 3                        # 32, 64 and 128 only
     assert call(dt=vd.F32, D=48) == 3
     assert call(q=Q + 8) == 5                     # VDIT_E_ALIGN
     assert call(o=Q + 16) == 6                    # VDIT_E_ALIAS (o inside q)
@@ -155,7 +155,7 @@ def test_window_argument_errors(lib):
     assert call(ww=-2) == 2
     assert call(T=0) == 2
     assert call(T=64, Hp=256, Wp=256, heads=16) == 2  # one batch over 2 GiB in bf16
-    assert call(D=32) == 3
+    assert call(D=48) == 3
     assert call(dt=vd.F32, D=80) == 3
     assert call(k=K + 8) == 5
     assert call(o=V + 16) == 6

@@ -53,6 +53,15 @@ SMALL = [
     # head_dim 64 over several key tiles: 250-token frames (4 tiles, the
     # last with 58 keys, so its second 32-key block is ragged).
     ("multi_tile_d64", 1, (3, 10, 25), 2, 64),
+    # head_dim 32 (16 rows per 1 KB tile load; the full pass on the 4-wave
+    # tile): ragged tiles, several key tiles, two clips with three query
+    # blocks, and the temporal kernel's 32-row slices (T = 7, 30, 33, 40).
+    ("ragged_d32", 2, (3, 7, 11), 2, 32),
+    ("multi_tile_d32", 1, (3, 10, 25), 2, 32),
+    ("two_clips_d32", 2, (5, 4, 31), 2, 32),
+    ("time_30_d32", 1, (30, 2, 3), 2, 32),
+    ("time_33_d32", 1, (33, 2, 3), 2, 32),
+    ("long_time_40_d32", 1, (40, 2, 3), 3, 32),
 ]
 
 
@@ -403,6 +412,8 @@ ROPE_SMALL = [
     # 40 frames: the temporal kernel's two-block form (T > 32).
     ("rope_long_time_40", 1, (40, 2, 3), 2, 128, (44, 42, 42)),
     ("rope_d64", 1, (5, 6, 9), 3, 64, (24, 20, 20)),
+    ("rope_d32", 1, (5, 6, 9), 3, 32, (12, 10, 10)),
+    ("rope_two_clips_d32", 2, (5, 4, 31), 2, 32, (12, 10, 10)),
     ("rope_uneven_split", 1, (3, 7, 11), 2, 128, (64, 32, 32)),
     ("rope_no_time_part", 1, (3, 7, 11), 2, 128, (0, 64, 64)),
 ]
@@ -577,7 +588,8 @@ CROSS_SMALL = [("cross_231x77", 2, 231, 77, 2, 128), ("cross_1000x512", 1, 1000,
                ("cross_d64", 1, 300, 130, 3, 64), ("cross_one_key", 2, 150, 1, 2, 128),
                # head_dim 64 over five key tiles, the last with 20 keys (a
                # fully masked second 32-key block).
-               ("cross_d64_5tiles", 1, 400, 276, 2, 64)]
+               ("cross_d64_5tiles", 1, 400, 276, 2, 64),
+               ("cross_d32", 1, 300, 130, 3, 32), ("cross_d32_5tiles", 2, 400, 276, 2, 32)]
 
 
 @pytest.mark.parametrize("case", CROSS_SMALL, ids=[c[0] for c in CROSS_SMALL])
@@ -639,6 +651,8 @@ WINDOW_SMALL = [
     ("larger_than_grid", 1, (3, 5, 7), (8, 16, 16), 2, 128),
     ("one_token", 1, (2, 3, 5), (1, 1, 1), 2, 128),
     ("thin_rows", 1, (2, 20, 70), (1, 1, 67), 2, 64),
+    ("d32", 1, (6, 7, 11), (4, 3, 6), 3, 32),
+    ("thin_rows_d32", 2, (2, 20, 70), (1, 1, 67), 2, 32),
 ]
 
 
