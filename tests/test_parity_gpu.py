@@ -248,6 +248,8 @@ def test_patchify_bias_chunks(C, dout):
     (3, 1, 2, 2, 448, 1),    # K = 12: W rows not a multiple of 8 elements; 7 channel steps
     (16, 2, 2, 2, 256, 1),   # K = 128: beyond the per-wavefront kernel's two k steps
     (8, 1, 2, 6, 384, 1),    # K = 96, six-wide bricks: general gather of the chunked kernel
+    (4, 1, 2, 2, 200, 1),    # 200 channels: the last 64-channel step holds 8
+    (16, 1, 2, 2, 840, 2),   # 840 channels: a third channel group of 72 (a full step and 8)
 ])
 def test_patchify_patch_lengths(C, pt, ph, pw, dout, B):
     # Patch lengths on both sides of 64 (the largest the per-wavefront kernel
@@ -257,7 +259,8 @@ def test_patchify_patch_lengths(C, pt, ph, pw, dout, B):
     d = draw(44 + C + pw, [("x", (B, C, 2 * pt, 5 * ph, 7 * pw), 1.0), ("w", (dout, C, pt, ph, pw), 0.05),
                            ("b", (dout,), 0.1)], "bf16")
     x, wt, b = (to_dev(d[n]) for n in ("x", "w", "b"))
-    got = to_host(vd.patchify(x, wt, b, heads=dout // 64, head_dim=64))
+    heads = dout // 64 if dout % 64 == 0 else dout // 8
+    got = to_host(vd.patchify(x, wt, b, heads=heads, head_dim=dout // heads))
     ref = oracle.patchify(d["x"].f32, d["w"].f32, d["b"].f32)
     assert got.shape == ref.shape == (B, 70, dout)
     assert_close(got, ref, "bf16", f"patchify/K{C * pt * ph * pw}")
