@@ -3,7 +3,7 @@ to a brute force that uses neither of them nor any other oracle routine.
 
 The chain is the "time then space" block of the "Video and 3D Generation"
 cheatsheet ("Tiny video DiT"; "Functions in the lessons": the divided
-attention block) and the block-input order of this build's 480p workload
+attention block) and the block-input order of the 480p block-input workload
 (spatial, then temporal). Each pass attends with q = k = RoPE(x) (or x with no
 split) and v = x, the order "How AI Generates Video ..." section 5 gives for
 attn1 (rotate Q and K, then attend).
