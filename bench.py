@@ -222,6 +222,7 @@ def main():
     }
 
     result["temporal_alone"] = bench_temporal_alone(vd, torch, qd, kd, vd_, ot, grid, b_temporal)
+    result["patchify_alone"] = bench_patchify_alone(vd, torch, lat, wgt, tok, wb, b_patch)
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch),
                            "rope_in_attention": bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_,
@@ -261,6 +262,26 @@ def bench_temporal_alone(vd, torch, q, k, v, o, grid, nbytes, iters: int = 20):
     a.record()
     for _ in range(iters):
         vd.attn_temporal(q, k, v, grid, out=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    return {"ms": ms, "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def bench_patchify_alone(vd, torch, lat, wgt, tok, wb, nbytes, iters: int = 20):
+    """Patchify launched back to back on the step's latent and weight. The
+    step's per-pass figure brackets a single ~20 us launch with a pair of
+    events, which adds their processing and the dispatch of the launch
+    (a few us) to the kernel's own time; here 20 launches run between one
+    pair of events, so each carries only the gap between consecutive
+    kernels. The 4 MB latent stays cached across launches; the bytes are
+    dominated by the 100.6 MB of tokens written."""
+    fn = lambda: vd.patchify(lat, wgt, heads=wb.heads, head_dim=wb.head_dim, out=tok)
+    _warm(torch, fn)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / iters
