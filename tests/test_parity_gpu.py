@@ -302,6 +302,21 @@ def test_480p_full_sampled():
     _sampled_attention("480p_full", "full", 512)
 
 
+@pytest.mark.parametrize("mode,stride", [("full", 1637), ("spatial", 389)])
+def test_480p_grid_d32_sampled(mode, stride):
+    # head_dim 32 at the 480p token grid (48 heads keep the 1,536 width): the
+    # full pass's whole-clip key loop, and every 1,560-key frame of the
+    # spatial pass, on the 4-wave tile that head_dim 32 uses.
+    grid = (21, 30, 52)
+    _announce(f"480p grid, 48 heads x 32, {mode}, rows every {stride}")
+    w = small_grid("d32_480p", 1 if mode == "full" else 2, *grid, 48, 32, "bf16", seed=33)
+    d, (q, k, v) = _qkv(w)
+    got = PASSES[mode](q, k, v, grid)
+    rows = sample_rows(w.N, stride, offset=stride // 2)
+    ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode, rows=rows)
+    assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", f"480p_d32/{mode}")
+
+
 def test_480p_divided_spatial_sampled():
     _sampled_attention("480p_divided", "spatial", 97)
 
