@@ -12,9 +12,10 @@
 // are HW tokens apart; the kernel addresses them in place, so the
 // time<->space permute is never materialised.
 //  * Q, K and V rows of the sequence go straight from HBM into the wave's
-//    own LDS slice with buffer loads that write LDS (each 1 KB load covers
-//    four whole 256-byte rows, so every request is a full cache line). The
-//    buffer descriptors end at row T-1, so the padding rows read as zeros.
+//    own LDS slice with non-temporal buffer loads that write LDS (each 1 KB
+//    load covers four whole 256-byte rows, so every request is a full
+//    cache line). The buffer descriptors end at row T-1, so the padding rows
+//    read as zeros.
 //    Each wave only ever reads its own slice, so waves never wait for each
 //    other: no workgroup barrier.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32x32 covers T <= 32; T <= 64
@@ -43,6 +44,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Buffer descriptor word 3 for gfx9-family raw (unswizzled) buffers.
 constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the Q/K/V loads: non-temporal (the NT bit). Every byte of
+// Q, K and V is read exactly once, and marked as streaming data the pass
+// runs at 5.8 TB/s instead of 5.1 (plain or non-temporal stores of O make no
+// difference, and non-temporal stores on top of these loads cost some of
+// the gain).
+constexpr int kStreamLoad = 2;
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory loads
 // (including the ones that write LDS directly) are still outstanding.
 template <int N>
@@ -141,14 +148,15 @@ __global__ __launch_bounds__(kWaves * 64) void temporal_bf16(
     for (int i = 0; i < QKR / RPL; ++i) {
         const int r = RPL * i + lane / CH, pc = lane % CH;
         const uint32_t off = (uint32_t)(r * fs * 2) + (pc ^ swz_k<D>(r, 0)) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qs_ + i * 1024), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(ks_ + i * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void *)(qs_ + i * 1024), 16, off, 0, 0, kStreamLoad);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void *)(ks_ + i * 1024), 16, off, 0, 0, kStreamLoad);
     }
 #pragma unroll
     for (int i = 0; i < TP / RPL; ++i) {
         const int r = RPL * i + lane / CH, pc = lane % CH;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void *)(vs_ + i * 1024), 16,
-                                                 (uint32_t)(r * fs * 2) + (pc ^ swz_v<D>(r, 0)) * 16, 0, 0, 0);
+                                                 (uint32_t)(r * fs * 2) + (pc ^ swz_v<D>(r, 0)) * 16, 0, 0,
+                                                 kStreamLoad);
     }
     // Loads complete in issue order: with only the TP/RPL V loads still
     // outstanding, this wave's Q and K rows are in its LDS slice.
