@@ -42,12 +42,19 @@ constexpr int kGroupT = 8;   // token tiles per ordering group
 constexpr int kRowBytes = kBK * 2;                  // 128 bytes of one tile row
 constexpr int kTileBytes = kTileC * kRowBytes;      // 32 KB (W or x tile)
 constexpr int kStageBytes = 2 * kTileBytes;         // W tile then x tile
-constexpr int kLdsBytes = 2 * kStageBytes;          // two stages: 128 KB
+constexpr int kStagesBytes = 2 * kStageBytes;       // two stages: 128 KB
+// After the stages: the tile's 256 biases and gains as fp32, and the RoPE
+// frequency of each (axis, lane half, register pair) slot of the epilogue,
+// zero where the pair turns with another axis.
+constexpr int kTabBytes = (2 * kTileC + 3 * 64) * 4;
+constexpr int kLdsBytes = kStagesBytes + kTabBytes;
 constexpr int kLoads = kTileBytes / 1024 / (kThreads / 64);  // 1 KB loads per wave per tile
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -89,6 +96,34 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
     const int wc = wave & 1, wt = wave >> 1;  // channel half, token quarter of the tile
+
+    // Epilogue tables (published by the first barrier below). Slot j of a
+    // lane half h is register pair rp = j % 8 of channel block cb = j / 8,
+    // i.e. pair cb*16 + 4*(rp/2) + rp%2 + 2h of the head; its angle is
+    // t*ft + h*fh + w*fw with two of the three frequencies zero.
+    lds_f32 *tbias = (lds_f32 *)(lds + kStagesBytes);
+    lds_f32 *tgain = tbias + kTileC;
+    lds_f32 *tfreq = tgain + kTileC;  // [axis][half][32]
+    {
+        const int c = tid & (kTileC - 1), cc = c0 + c;
+        if (tid < kTileC) {
+            tbias[c] = bias && cc < 3 * dim ? __uint_as_float((uint32_t)bias[cc] << 16) : 0.f;
+        } else {
+            float gv = 1.f;
+            if (cc < dim) {
+                if (gq) gv = __uint_as_float((uint32_t)gq[cc] << 16);
+            } else if (cc < 2 * dim) {
+                if (gk) gv = __uint_as_float((uint32_t)gk[cc - dim] << 16);
+            }
+            tgain[c] = gv;
+        }
+        if (tid < 3 * 64) {
+            const int ax = tid >> 6, h = (tid >> 5) & 1, j = tid & 31;
+            const int pr = (j >> 3) * 16 + 4 * ((j & 7) >> 1) + (j & 1) + 2 * h;
+            const bool on = ax == 0 ? pr < rope.b1 : (ax == 1 ? pr >= rope.b1 && pr < rope.b2 : pr >= rope.b2);
+            tfreq[tid] = on ? rope.freq_rev[pr] : 0.f;
+        }
+    }
 
     // Buffer descriptors from the tile's first W row and first x row; the
     // sizes end at the last row of each matrix.
@@ -189,25 +224,20 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
     // Lane channels within the head: cb*32 + 8*r4 + 4*half + e, e < 4 (the
     // accumulator register 4*r4 + e of block cb). Every 32-token block is
     // finished in registers, staged through this wave's own LDS region and
-    // written as whole 256-byte token rows. Bias and gain are read per
-    // block (from L2) rather than held across both blocks, which would
-    // spill at two waves per SIMD.
+    // written as whole 256-byte token rows. Bias, gain and the RoPE
+    // frequencies come from the fp32 tables in LDS, four per read.
     const int cw = c0 + wc * 128;
     if (cw >= 3 * dim) return;
     const int which = cw / dim;             // 0 Q, 1 K, 2 V
     const int hc = cw - which * dim;        // first channel of the head within its tensor
     uint16_t *out = which == 0 ? q : (which == 1 ? k : v);
-    const uint16_t *gain = which == 0 ? gq : (which == 1 ? gk : nullptr);
+    const bool norm = which == 0 ? gq != nullptr : (which == 1 ? gk != nullptr : false);
     const bool rot = which < 2 && rope.on;
     const int HW = g.Hp * g.Wp;
-
-    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
-    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
-    // RoPE: pair rp of block cb is channel pair p = cb*16 + 4*(rp/2) + rp%2
-    // + 2*half; pairs below rope.b1 turn with t, below rope.b2 with h, the
-    // rest with w.
     constexpr int kPitch = 272;  // bytes per staged token row (256 + 16 keeps writes conflict-free)
     lds_u8 *stg = lds + wave * 32 * kPitch;
+    const lds_f32 *wbias = tbias + wc * 128 + 4 * half, *wgain = tgain + wc * 128 + 4 * half;
+    const lds_f32 *wfreq = tfreq + 32 * half;
 
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
@@ -215,30 +245,31 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
         const int m = mt + col;
         float y[4][16];
         float ss = 0.f;
+        // Lane channels of block cb, registers 4*r4 .. 4*r4+3: head channels
+        // cb*32 + 8*r4 + 4*half .. +3.
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
-                const int ch = cb * 32 + 8 * r4 + 4 * half;
-                const u32x2 bw = bias ? *(const u32x2 *)(bias + cw + ch) : (u32x2){0u, 0u};
-                const float b4[4] = {lo(bw[0]), hi(bw[0]), lo(bw[1]), hi(bw[1])};
+                const f32x4 b4 = *(const lds_f32x4 *)(wbias + cb * 32 + 8 * r4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     y[cb][4 * r4 + e] = acc[cb][tb][4 * r4 + e] + b4[e];
                     ss = fmaf(y[cb][4 * r4 + e], y[cb][4 * r4 + e], ss);
                 }
             }
-        if (gain) {
-            const float sc = __builtin_amdgcn_rsqf(pair_sum(ss) * (1.0f / 128.0f) + g.eps);
+        // RMSNorm: the gain now, the token's 1/rms after the rotation
+        // (which is linear and acts within the token).
+        float rs = 1.f;
+        if (norm) {
+            rs = __builtin_amdgcn_rsqf(pair_sum(ss) * (1.0f / 128.0f) + g.eps);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int ch = cb * 32 + 8 * r4 + 4 * half;
-                    const u32x2 gw = *(const u32x2 *)(gain + hc + ch);
-                    const float g4[4] = {lo(gw[0]), hi(gw[0]), lo(gw[1]), hi(gw[1])};
+                    const f32x4 g4 = *(const lds_f32x4 *)(wgain + cb * 32 + 8 * r4);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) y[cb][4 * r4 + e] *= sc * g4[e];
+                    for (int e = 0; e < 4; ++e) y[cb][4 * r4 + e] *= g4[e];
                 }
         }
         if (rot) {
@@ -247,19 +278,28 @@ __global__ __launch_bounds__(kThreads, 1) void qkv_proj_bf16(
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-                for (int rp = 0; rp < 8; ++rp) {
-                    const int p0 = cb * 16 + 4 * (rp >> 1) + (rp & 1);
-                    const int pr = p0 + 2 * half;
-                    const float pos = pr < rope.b1 ? pt : (pr < rope.b2 ? ph : pw);
-                    const float fq = half ? rope.freq_rev[p0 + 2] : rope.freq_rev[p0];
-                    // Angle in revolutions, reduced to [0, 1) for v_sin/v_cos.
-                    const float rev = __builtin_amdgcn_fractf(pos * fq);
-                    const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
-                    const int r = 2 * rp;
-                    const float re = y[cb][r], im = y[cb][r + 1];
-                    y[cb][r] = re * cs - im * sn;
-                    y[cb][r + 1] = re * sn + im * cs;
+                for (int rq = 0; rq < 2; ++rq) {
+                    const int j = cb * 8 + 4 * rq;
+                    const f32x4 ft = *(const lds_f32x4 *)(wfreq + j);
+                    const f32x4 fh = *(const lds_f32x4 *)(wfreq + 64 + j);
+                    const f32x4 fw = *(const lds_f32x4 *)(wfreq + 128 + j);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // Angle in revolutions, reduced to [0, 1) for v_sin/v_cos.
+                        const float rev = __builtin_amdgcn_fractf(fmaf(pw, fw[i], fmaf(ph, fh[i], pt * ft[i])));
+                        const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                        const int r = 2 * (4 * rq + i);
+                        const float re = y[cb][r], im = y[cb][r + 1];
+                        y[cb][r] = re * cs - im * sn;
+                        y[cb][r + 1] = re * sn + im * cs;
+                    }
                 }
+        }
+        if (norm) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[cb][r] *= rs;
         }
         // Stage: token col's row, channels cb*32 + 8*r4 + 4*half .. +3.
 #pragma unroll
