@@ -756,6 +756,10 @@ QKV_SMALL = [
     # A wide grid: w positions up to 199, so the w-axis angles reach many
     # revolutions before their reduction.
     ("wide_grid_rope", 1, (1, 2, 200), 2, 128, "bf16", (44, 42, 42), True, True),
+    # Five heads: 1,920 channels in 7.5 tiles of 256, so one tile holds the
+    # last Q heads and the first K heads and another the last K heads and
+    # the first V heads (per-channel bias, gain and rotation across them).
+    ("five_heads_rope", 1, (3, 4, 10), 5, 128, "bf16", (44, 42, 42), True, True),
 ]
 
 
