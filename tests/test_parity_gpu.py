@@ -302,19 +302,22 @@ def test_480p_full_sampled():
     _sampled_attention("480p_full", "full", 512)
 
 
-@pytest.mark.parametrize("mode,stride", [("full", 1637), ("spatial", 389)])
-def test_480p_grid_d32_sampled(mode, stride):
-    # head_dim 32 at the 480p token grid (48 heads keep the 1,536 width): the
-    # full pass's whole-clip key loop, and every 1,560-key frame of the
-    # spatial pass, on the 4-wave tile that head_dim 32 uses.
+@pytest.mark.parametrize("D,mode,stride", [(32, "full", 1637), (32, "spatial", 389), (32, "temporal", 97),
+                                            (64, "full", 1637), (64, "spatial", 389), (64, "temporal", 97)])
+def test_480p_grid_small_heads_sampled(D, mode, stride):
+    # head_dim 32 and 64 at the 480p token grid (1536 / D heads keep the
+    # width): the full pass's whole-clip key loop (head_dim 64 on the 8-wave
+    # ping-pong, 32 on the 4-wave tile), every 1,560-key frame of the spatial
+    # pass, and the 21-frame temporal sequences.
     grid = (21, 30, 52)
-    _announce(f"480p grid, 48 heads x 32, {mode}, rows every {stride}")
-    w = small_grid("d32_480p", 1 if mode == "full" else 2, *grid, 48, 32, "bf16", seed=33)
+    heads = 1536 // D
+    _announce(f"480p grid, {heads} heads x {D}, {mode}, rows every {stride}")
+    w = small_grid(f"d{D}_480p", 1 if mode == "full" else 2, *grid, heads, D, "bf16", seed=33 + D)
     d, (q, k, v) = _qkv(w)
     got = PASSES[mode](q, k, v, grid)
     rows = sample_rows(w.N, stride, offset=stride // 2)
     ref = oracle.attention(d["q"].f32, d["k"].f32, d["v"].f32, grid, mode, rows=rows)
-    assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", f"480p_d32/{mode}")
+    assert_close(to_host(got[:, torch.from_numpy(rows).cuda()]), ref, "bf16", f"480p_d{D}/{mode}")
 
 
 def test_480p_divided_spatial_sampled():
