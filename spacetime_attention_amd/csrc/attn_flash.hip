@@ -171,7 +171,9 @@ __device__ __forceinline__ u32x4 rope_chunk(u32x4 x, int lc, float pt, float ph,
 // 32-key blocks from the K tile at LDS byte offset KB0; flash_softmax takes
 // the online softmax over those scores (kvalid = number of the tile's keys
 // that exist) and leaves the probabilities P^T as bf16 MFMA operands;
-// flash_pv adds V^T P^T to O^T from the V tile at LDS byte offset VB0.
+// flash_pv adds V^T P^T to O^T from the V tile VB0 bytes past the per-lane
+// read bases vbase (row and column of the lane's transposed reads, plus
+// the start of the V buffers).
 template <int D, int QB>
 __device__ __forceinline__ void flash_s(const lds_u8 *lds, uint32_t KB0, const uint32_t (&kofs)[D / 16],
                                         const bf16x8 (&qop)[QB][D / 16], f32x16 (&sacc)[2][QB])
@@ -303,19 +305,18 @@ __device__ __forceinline__ void flash_softmax(f32x16 (&sacc)[2][QB], bf16x8 (&po
 }
 
 template <int D, int QB>
-__device__ __forceinline__ void flash_pv(const lds_u8 *lds, uint32_t VB0, const uint32_t (&vofs)[D / 32],
+__device__ __forceinline__ void flash_pv(const lds_u8 *lds, uint32_t VB0, const uint32_t (&vbase)[D / 32],
                                          const bf16x8 (&pop)[QB][2][2], f32x16 (&oacc)[D / 32][QB])
 {
     constexpr int DB = D / 32;
     constexpr int RB = D * 2;  // bytes per row
-    constexpr int TILE = kBN * RB;
     bf16x4 va[2][DB][2];
     auto rdv = [&](int st, int slot) {
         const uint32_t off = VB0 + ((st >> 1) * 32 + 16 * (st & 1)) * RB;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            va[slot][db][0] = lds_read_tr(lds + (vofs[db] - TILE) + off);
-            va[slot][db][1] = lds_read_tr(lds + (vofs[db] - TILE) + (off + 8 * RB));
+            va[slot][db][0] = lds_read_tr(lds + vbase[db] + off);
+            va[slot][db][1] = lds_read_tr(lds + vbase[db] + (off + 8 * RB));
         }
     };
     rdv(0, 0);
@@ -790,6 +791,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
         // before the barrier that ends Y(j), ahead of their first reader.
         const bool late = wave >= 4;
         constexpr uint32_t VB = 3 * S::TILE;  // V buffers follow the K buffers
+        // Per-lane bases of the transposed V reads, including the start of
+        // the V buffers, kept opaque so that the compiler leaves the buffer
+        // and row constants (all below 64 KB from here) in the reads'
+        // offset fields instead of forming an address per read.
+        uint32_t vbase[S::DB];
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+            vbase[db] = vofs[db] - S::TILE + VB;
+            asm volatile("" : "+v"(vbase[db]));
+        }
         f32x16 sacc[2][QB];
         bf16x8 pop[QB][2][2];
         load_one(krs, koff, 0, 0);
@@ -807,7 +818,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void flash_fwd_bf16(
             constexpr uint32_t bp = (b + 2) % 3, b1 = (b + 1) % 3, b2 = (b + 2) % 3;
             // X(j)
             if (busy) {
-                if (j > 0) flash_pv<D, QB>(lds, VB + bp * S::TILE, vofs, pop, oacc);
+                if (j > 0) flash_pv<D, QB>(lds, bp * S::TILE, vbase, pop, oacc);
                 if (j < ntiles) flash_s<D, QB>(lds, b * S::TILE, kofs, qop, sacc);
             }
             lds_barrier();
