@@ -58,9 +58,12 @@ def _dev(d):
     return torch.from_numpy(np.ascontiguousarray(d.bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _source_hash(name: str) -> str:
-    path = os.path.join(ROOT, "spacetime_attention_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def _source_hash(names: str) -> str:
+    """sha256 (16 hex digits) of the "+"-joined kernel sources, concatenated."""
+    h = hashlib.sha256()
+    for name in names.split("+"):
+        h.update(open(os.path.join(ROOT, "spacetime_attention_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel_file: str, per_launch_key: str):
@@ -194,7 +197,7 @@ def main():
     roofline = {"kernel": "flash_fwd_bf16<128,1,8,0> (vdit_attn_full, 480p)", "bound": "mfma",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": _traffic("attn_flash.hip", "flash_full_480p")}
+                "traffic": _traffic("attn_flash_kernel.h+attn_flash_full.hip", "flash_full_480p")}
 
     result = {
         "metric": METRIC,

@@ -19,8 +19,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libvdit.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["attn_flash.hip", "attn_temporal.hip", "attn_f32.hip", "patchify.hip", "rope3d.hip", "qkv_proj.hip",
-           "vdit_abi.hip"]
+SOURCES = ["attn_flash.hip", "attn_flash_full.hip", "attn_temporal.hip", "attn_f32.hip", "patchify.hip",
+           "rope3d.hip", "qkv_proj.hip", "vdit_abi.hip"]
+# Per-file flags. The full pass's ping-pong kernel is scheduled with LLVM's
+# maximum-ILP strategy (measured faster there, slower on the other passes).
+FILE_FLAGS = {"attn_flash_full.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -33,7 +36,7 @@ FLAGS = [
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

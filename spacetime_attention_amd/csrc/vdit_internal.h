@@ -75,6 +75,10 @@ struct FlashRope {
 hipError_t launch_flash_rope_bf16(const void *q, const void *k, const void *v, void *o, int nseg, int L, int Lk,
                                   int heads, int D, float scale_log2e, int pass, const FlashRope &rope,
                                   hipStream_t s);
+// Full attention at head_dim 64 or 128 (nseg = B clips of N tokens) on the
+// 8-wavefront ping-pong kernel; rope as launch_flash_rope_bf16, or null.
+hipError_t launch_flash_full_bf16(const void *q, const void *k, const void *v, void *o, int B, int N, int heads,
+                                  int D, float scale_log2e, const FlashRope *rope, hipStream_t s);
 
 // Non-overlapping spacetime windows over a (T, Hp, Wp) token grid: window
 // (iwt, iwh, iww) holds tokens t in [iwt*wt, min((iwt+1)*wt, T)) and likewise
