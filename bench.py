@@ -226,6 +226,9 @@ def main():
 
     result["temporal_alone"] = bench_temporal_alone(vd, torch, qd, kd, vd_, ot, grid, b_temporal)
     result["patchify_alone"] = bench_patchify_alone(vd, torch, lat, wgt, tok, wb, b_patch)
+    # Six cold [1,32760,12,128] inputs: the two batch halves of the divided Q, K and V.
+    rope_srcs = [t[i:i + 1] for t in (qd, kd, vd_) for i in range(2)]
+    result["rope_alone"] = bench_rope_alone(vd, torch, rope_srcs, rot, grid, wb.rope_split, b_rope)
     result["next_rows"] = {"cross": bench_cross(vd, torch), "window": bench_window(vd, torch),
                            "qkv_proj": bench_qkv(vd, torch),
                            "rope_in_attention": bench_rope_in_attention(vd, torch, qf, kf, vf, of, qd, kd, vd_,
@@ -280,6 +283,28 @@ def bench_patchify_alone(vd, torch, lat, wgt, tok, wb, nbytes, iters: int = 20):
     kernels. The 4 MB latent stays cached across launches; the bytes are
     dominated by the 100.6 MB of tokens written."""
     fn = lambda: vd.patchify(lat, wgt, heads=wb.heads, head_dim=wb.head_dim, out=tok)
+    _warm(torch, fn)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    return {"ms": ms, "gbs": nbytes / ms / 1e6, "frac_hbm_peak": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+
+
+def bench_rope_alone(vd, torch, srcs, out, grid, split, nbytes, iters: int = 24):
+    """3D RoPE launched back to back, like patchify_alone, so each launch
+    carries only the gap between kernels instead of an event pair. The
+    launches cycle over six distinct 100.6 MB inputs (600 MB, more than the
+    256 MB Infinity Cache), so every launch reads its input from HBM."""
+    k = [0]
+
+    def fn():
+        vd.rope3d(srcs[k[0] % len(srcs)], grid, split, out=out)
+        k[0] += 1
+
     _warm(torch, fn)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
